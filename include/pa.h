@@ -1,0 +1,219 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention library, libpa.so.
+ *
+ * Paged attention is softmax attention computed directly over a K/V cache
+ * that is scattered into fixed-size physical blocks and reached through a
+ * per-sequence block table (JuliaPagedAttn README, "Architecture" and
+ * "Block Layout"; Pico-vLLM #5 Paged Attention, "核心数据结构和设计模式";
+ * nanoserve Day 19, "What I added today").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument named as device memory must point to memory the
+ *   caller allocated on the current HIP device; the library never allocates,
+ *   frees or keeps a pointer after a call returns.  Host pointers (the
+ *   descriptor structs themselves) are only read during the call.
+ * - Work is enqueued on `stream` (NULL = the default stream) and runs
+ *   asynchronously; a PA_OK return means the launch was accepted.
+ * - Arguments are checked on the host before anything is enqueued.  A
+ *   failed check returns PA_ERR_INVALID_ARG or PA_ERR_UNSUPPORTED and
+ *   enqueues nothing; pa_last_error() then describes the failed check.
+ *   The contents of device arrays (tables, lengths, slots) are not read on
+ *   the host; the kernels treat out-of-range entries as described per call
+ *   and never access memory outside the buffers described here.
+ * - Indices are 0-based.  Element types: PA_F32 is IEEE binary32, PA_BF16 is
+ *   bfloat16 (the high 16 bits of a binary32).  q, out, k_new and v_new use
+ *   the pool's element type.
+ * - The library keeps no state between calls apart from thread-local error
+ *   text, so calls from several host threads are safe.  Calls that write
+ *   the same device memory must be ordered by the caller (one stream).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as the HIP runtime's, so either header may come first. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer ... */
+  PA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels cover  */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
+  PA_ERR_HIP = -4           /* the HIP runtime refused a launch              */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_BF16 = 1
+} pa_dtype;
+
+/*
+ * The block pool of one attention layer.
+ *
+ * k_cache and v_cache (device) are each a row-major, contiguous array
+ * [num_blocks, block_size, num_kv_heads, head_dim] of `dtype` -- the
+ * Pico-vLLM pool tensor [2, num_layers, num_blocks, block_size,
+ * num_kv_heads, head_dim] ("核心数据结构和设计模式", BlockManager listing)
+ * with its K/V and layer indices fixed; a multi-layer pool is passed one
+ * layer at a time as two base pointers.  One block table addresses both
+ * pools.  Both pointers must be 16-byte aligned.
+ *
+ * Supported: block_size 16, head_dim 64 or 128, dtype PA_F32 or PA_BF16.
+ */
+typedef struct pa_kv_pool {
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_kv_pool;
+
+/*
+ * The sequences of a batch.
+ *
+ * block_tables (device, int32 [num_seqs, max_blocks_per_seq], row-major):
+ *   physical block ids, the fixed-width form of Pico-vLLM's int32
+ *   get_block_table() ("核心数据结构和设计模式").  Entry j of row s holds
+ *   positions j*block_size .. (j+1)*block_size-1 of sequence s.  Entries at
+ *   or past ceil(context_lens[s] / block_size) are never read.  Several rows
+ *   may name the same physical block (copy-on-write sharing of a prefix,
+ *   JuliaPagedAttn "Copy-on-Write").
+ * context_lens (device, int32 [num_seqs]): tokens of each sequence already in
+ *   the pool, counting the one written in the current step (Pico-vLLM's +1
+ *   rule; JuliaPagedAttn's `context_lengths`).
+ * max_context_len (host): an upper bound of context_lens used to size the
+ *   launch.  Kernels use min(context_lens[s], max_context_len,
+ *   max_blocks_per_seq * block_size) as the context length, so a violated
+ *   bound truncates instead of reading out of bounds.
+ */
+typedef struct pa_seq_desc {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+} pa_seq_desc;
+
+/*
+ * pa_slot_mapping -- pool slot of each new token.
+ *
+ * Token i belongs to sequence s and is one of its q_len newest positions:
+ *   without q_start_loc (NULL): num_tokens == num_seqs, token i is the last
+ *     position context_lens[i]-1 of sequence i (decode);
+ *   with q_start_loc (device, int32 [num_seqs+1], non-decreasing, first 0):
+ *     sequence s owns tokens q_start_loc[s] .. q_start_loc[s+1]-1, q_len =
+ *     q_start_loc[s+1]-q_start_loc[s], and token q_start_loc[s]+i sits at
+ *     position context_lens[s] - q_len + i (prefill, or a chunk of one).
+ * slot_mapping (device, int64 [num_tokens], written):
+ *   block_tables[s][pos / block_size] * block_size + pos % block_size, the
+ *   flat row of the token in the pool viewed as [num_blocks * block_size,
+ *   num_kv_heads, head_dim] (JuliaPagedAttn "Project Structure": slot mapping
+ *   in the cache layout; nanoserve Day 19 "Diagram": slot_mapping).  -1 where
+ *   the position is negative, at or past the context, past the table width,
+ *   or the table entry is not a block of the pool.
+ */
+pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                          const int32_t* q_start_loc, int32_t num_tokens,
+                          int64_t* slot_mapping, hipStream_t stream);
+
+/*
+ * pa_write_kv -- scatter this step's K/V rows into the pool.
+ *
+ * k_new, v_new (device, [num_tokens, num_kv_heads, head_dim] of the pool's
+ * dtype, 16-byte aligned) are copied bit for bit into row slot_mapping[t] of
+ * k_cache and v_cache (JuliaPagedAttn "API Reference": write_kv_cache!;
+ * nanoserve Day 19 "What I added today": the write of this step's K/V to its
+ * slots).  Slots below 0 or at or past num_blocks * block_size are skipped.
+ * Two tokens with the same slot race (the caller's responsibility).
+ */
+pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int32_t num_tokens,
+                      hipStream_t stream);
+
+/*
+ * pa_decode_workspace_bytes -- device workspace pa_decode needs.
+ *
+ * 0 when one partition covers max_context_len (partition_size 0 or >=
+ * the longest context): the kernel then writes `out` directly.  Host only;
+ * returns 0 for invalid arguments too (pa_decode then reports them).
+ */
+size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode -- attention of one new query row per (sequence, query head)
+ * over the sequence's whole paged history.
+ *
+ * out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K_s[t, h / n_rep, :])
+ *                * V_s[t, h / n_rep, :]
+ * with t = 0 .. context_len-1 read through block_tables and n_rep =
+ * num_q_heads / num_kv_heads (GQA: the compact KV heads are repeated to the
+ * query heads at read time, nanoserve Day 19 "What I learned" item 4).
+ * The softmax is computed online with a running maximum and running sum
+ * (JuliaPagedAttn "Online Softmax"); a context of length 0 gives zeros.
+ *
+ * q (device, [num_seqs, num_q_heads, head_dim]) and out (device, same shape)
+ * are in the pool's dtype, 16-byte aligned; out is rounded to nearest even
+ * for bf16.  Accumulation is fp32.
+ *
+ * partition_size: 0 = one pass per (sequence, KV head).  Otherwise a multiple
+ * of block_size: each sequence's context is split into partitions of that
+ * many tokens that are processed in parallel, each keeping its own maximum,
+ * sum and normalised output, and a second kernel merges them by
+ * log-sum-exp weighting.  The workspace (device, 256-byte aligned, at least
+ * pa_decode_workspace_bytes(...)) holds the per-partition results; its
+ * contents on entry do not matter.
+ *
+ * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
+                    void* out, int32_t num_q_heads, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_prefill -- causal attention of every new token of every sequence over
+ * its paged history, in one call (JuliaPagedAttn "Features": batched
+ * prefill, all prompt positions processed in a single kernel call).
+ *
+ * q (device, [total_q_tokens, num_q_heads, head_dim]) and out (same shape)
+ * are in the pool's dtype, 16-byte aligned.  q_start_loc (device, int32
+ * [num_seqs+1]) lists each sequence's tokens as in pa_slot_mapping; token
+ * q_start_loc[s]+i sits at position p = context_lens[s] - q_len + i and
+ * attends to positions 0 .. p of its sequence (the K/V of the new tokens must
+ * already be in the pool: pa_write_kv first).  max_q_len (host) bounds every
+ * q_len and sizes the launch; a longer q_len is truncated to it.
+ *
+ * Supported: PA_BF16 pools, head_dim 128, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}.  QK^T and PV run on bf16 matrix cores with fp32
+ * accumulation; the probabilities are rounded to bf16 for the PV product.
+ */
+pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
+                     void* out, const int32_t* q_start_loc, int32_t total_q_tokens,
+                     int32_t max_q_len, int32_t num_q_heads, float scale,
+                     hipStream_t stream);
+
+/* Static text naming a status code. */
+const char* pa_status_string(int32_t status);
+
+/* Thread-local text describing the last failed check or HIP error of this
+ * thread ("" if none).  Valid until the next call on the same thread. */
+const char* pa_last_error(void);
+
+/* Library ABI version: (major << 16) | minor. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,251 @@
+"""ctypes binding of libpa.so (``include/pa.h``).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape and contiguity, turned into raw pointers and handed to the C entry
+point of the same name on the current torch stream.  Every computation runs
+in the library's HIP kernels.  There is no fallback: if ``libpa.so`` is not
+built, importing the functions raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_HIP = -4
+PA_F32 = 0
+PA_BF16 = 1
+
+EXPORTED = (
+    "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill",
+    "pa_status_string", "pa_last_error", "pa_version",
+)
+
+
+class PaKVPool(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class PaSeqDesc(ctypes.Structure):
+    _fields_ = [
+        ("block_tables", ctypes.c_void_p),
+        ("context_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+    ]
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, call: str, status: int, detail: str):
+        super().__init__(f"{call} failed: {status_name(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_87_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pool_p, seq_p = ctypes.POINTER(PaKVPool), ctypes.POINTER(PaSeqDesc)
+    sig = {
+        "pa_slot_mapping": (i32, [pool_p, seq_p, vp, i32, vp, vp]),
+        "pa_write_kv": (i32, [pool_p, vp, vp, vp, i32, vp]),
+        "pa_decode_workspace_bytes": (sz, [seq_p, i32, i32, i32, i32]),
+        "pa_decode": (i32, [pool_p, seq_p, vp, vp, i32, f32, i32, vp, sz, vp]),
+        "pa_prefill": (i32, [pool_p, seq_p, vp, vp, vp, i32, i32, i32, f32, vp]),
+        "pa_status_string": (ctypes.c_char_p, [i32]),
+        "pa_last_error": (ctypes.c_char_p, []),
+        "pa_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load_library().pa_status_string(status).decode()
+
+
+def _check(call: str, status: int) -> None:
+    if status != PA_OK:
+        raise PagedAttentionError(call, status, load_library().pa_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PA_F32
+    if t == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported element type {t} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+@dataclass
+class KVPool:
+    """K and V pools of one layer: ``[num_blocks, block_size, num_kv_heads,
+    head_dim]`` each, same dtype, on the GPU."""
+
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+
+    def __post_init__(self):
+        if self.k_cache.shape != self.v_cache.shape or self.k_cache.dtype != self.v_cache.dtype:
+            raise ValueError("k_cache and v_cache must have the same shape and dtype")
+        if self.k_cache.dim() != 4:
+            raise ValueError("pools are [num_blocks, block_size, num_kv_heads, head_dim]")
+
+    def c(self) -> PaKVPool:
+        N, B, H, D = self.k_cache.shape
+        return PaKVPool(_dev(self.k_cache, "k_cache"), _dev(self.v_cache, "v_cache"), N, B, H, D,
+                        _dtype_code(self.k_cache.dtype))
+
+    @property
+    def dtype(self):
+        return self.k_cache.dtype
+
+
+@dataclass
+class SeqDesc:
+    """Block tables ``int32 [S, max_blocks_per_seq]`` and context lengths
+    ``int32 [S]`` on the GPU, plus a host-side bound of the lengths."""
+
+    block_tables: torch.Tensor
+    context_lens: torch.Tensor
+    max_context_len: int
+
+    def c(self) -> PaSeqDesc:
+        if self.block_tables.dim() != 2:
+            raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+        S, W = self.block_tables.shape
+        if self.context_lens.shape != (S,):
+            raise ValueError("context_lens must be [num_seqs]")
+        return PaSeqDesc(_dev(self.block_tables, "block_tables", torch.int32),
+                         _dev(self.context_lens, "context_lens", torch.int32), S, W,
+                         int(self.max_context_len))
+
+
+def pa_slot_mapping(pool: KVPool, seqs: SeqDesc, slot_mapping: torch.Tensor,
+                    q_start_loc: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    lib = load_library()
+    qsl = 0 if q_start_loc is None else _dev(q_start_loc, "q_start_loc", torch.int32)
+    cp, cs = pool.c(), seqs.c()
+    st = lib.pa_slot_mapping(ctypes.byref(cp), ctypes.byref(cs), qsl or None,
+                             slot_mapping.numel(), _dev(slot_mapping, "slot_mapping", torch.int64),
+                             _stream(stream))
+    _check("pa_slot_mapping", st)
+    return slot_mapping
+
+
+def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
+                slot_mapping: torch.Tensor, stream=None) -> None:
+    lib = load_library()
+    _, _, H, D = pool.k_cache.shape
+    T = slot_mapping.numel()
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{name} must be [{T}, {H}, {D}], got {tuple(t.shape)}")
+    cp = pool.c()
+    st = lib.pa_write_kv(ctypes.byref(cp), _dev(k_new, "k_new", pool.dtype),
+                         _dev(v_new, "v_new", pool.dtype),
+                         _dev(slot_mapping, "slot_mapping", torch.int64), T, _stream(stream))
+    _check("pa_write_kv", st)
+
+
+def pa_decode_workspace_bytes(seqs: SeqDesc, num_q_heads: int, head_dim: int, block_size: int,
+                              partition_size: int) -> int:
+    cs = seqs.c()
+    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(cs), num_q_heads, head_dim,
+                                                        block_size, partition_size))
+
+
+def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, scale: float,
+              partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    lib = load_library()
+    S, Hq, D = q.shape
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must have q's shape")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    cp, cs = pool.c(), seqs.c()
+    st = lib.pa_decode(ctypes.byref(cp), ctypes.byref(cs), _dev(q, "q", pool.dtype),
+                       _dev(out, "out", pool.dtype), Hq, float(scale), int(partition_size),
+                       ws_ptr, ws_bytes, _stream(stream))
+    _check("pa_decode", st)
+    return out
+
+
+def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
+               q_start_loc: torch.Tensor, max_q_len: int, scale: float,
+               stream=None) -> torch.Tensor:
+    lib = load_library()
+    T, Hq, D = q.shape
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must have q's shape")
+    cp, cs = pool.c(), seqs.c()
+    st = lib.pa_prefill(ctypes.byref(cp), ctypes.byref(cs), _dev(q, "q", pool.dtype),
+                        _dev(out, "out", pool.dtype), _dev(q_start_loc, "q_start_loc", torch.int32),
+                        T, int(max_q_len), Hq, float(scale), _stream(stream))
+    _check("pa_prefill", st)
+    return out
+
+
+def pa_version() -> int:
+    return int(load_library().pa_version())
+
+
+__all__ = [
+    "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
+    "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
+    "pa_decode", "pa_prefill", "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
+    "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_F32", "PA_BF16",
+]

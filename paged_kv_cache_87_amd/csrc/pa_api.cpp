@@ -1,0 +1,280 @@
+// C-ABI entry points of libpa.so: host-side argument checks, the decode
+// partition plan and the mapping of HIP errors to status codes.  Every
+// check runs before anything is enqueued; no entry point allocates.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_size(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+pa_status check_pool(const pa_kv_pool* pool) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "pool descriptor is null");
+  if (pool->k_cache == nullptr || pool->v_cache == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "k_cache or v_cache is null");
+  if (!aligned16(pool->k_cache) || !aligned16(pool->v_cache))
+    return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+  if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0 ||
+      pool->block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "pool sizes must be positive (num_blocks=%d block_size=%d "
+                "num_kv_heads=%d head_dim=%d)", pool->num_blocks, pool->block_size,
+                pool->num_kv_heads, pool->head_dim);
+  if (pool->dtype != PA_F32 && pool->dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", pool->dtype);
+  if (pool->block_size != pa::kBlockSize)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", pool->block_size);
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", pool->head_dim);
+  return PA_OK;
+}
+
+pa_status check_seqs(const pa_seq_desc* seqs) {
+  if (seqs == nullptr) return fail(PA_ERR_INVALID_ARG, "sequence descriptor is null");
+  if (seqs->num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", seqs->num_seqs);
+  if (seqs->num_seqs > 0 && (seqs->block_tables == nullptr || seqs->context_lens == nullptr))
+    return fail(PA_ERR_INVALID_ARG, "block_tables or context_lens is null");
+  if (seqs->max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d must be positive",
+                seqs->max_blocks_per_seq);
+  if (seqs->max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len %d < 0", seqs->max_context_len);
+  if (static_cast<int64_t>(seqs->max_blocks_per_seq) * pa::kBlockSize > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq too large");
+  return PA_OK;
+}
+
+pa_status check_heads(const pa_kv_pool* pool, int32_t num_q_heads) {
+  if (num_q_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d", num_q_heads);
+  if (num_q_heads % pool->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  const int n_rep = num_q_heads / pool->num_kv_heads;
+  if (n_rep != 1 && n_rep != 2 && n_rep != 4 && n_rep != 8)
+    return fail(PA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads = %d (supported: 1, 2, 4, 8)",
+                n_rep);
+  return PA_OK;
+}
+
+int32_t context_cap(const pa_seq_desc* seqs) {
+  const int64_t by_table = static_cast<int64_t>(seqs->max_blocks_per_seq) * pa::kBlockSize;
+  return static_cast<int32_t>(seqs->max_context_len < by_table ? seqs->max_context_len : by_table);
+}
+
+}  // namespace
+
+namespace pa {
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       int32_t num_q_heads, int32_t head_dim, int32_t partition_size) {
+  DecodePlan p{};
+  const int64_t by_table = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
+  p.context_cap = static_cast<int32_t>(max_context_len < by_table ? max_context_len : by_table);
+  const int32_t cover = ((p.context_cap > 0 ? p.context_cap : 1) + kBlockSize - 1) /
+                        kBlockSize * kBlockSize;
+  if (partition_size <= 0 || partition_size >= cover) {
+    p.partition_size = cover;
+    p.num_partitions = 1;
+  } else {
+    p.partition_size = partition_size;
+    p.num_partitions = (p.context_cap + partition_size - 1) / partition_size;
+  }
+  if (p.num_partitions > 1) {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.num_partitions;
+    const size_t o_bytes = rows * head_dim * sizeof(float);
+    p.part_ml_offset = (o_bytes + 255) / 256 * 256;
+    p.workspace_bytes = p.part_ml_offset + rows * 2 * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int32_t pa_version(void) { return (1 << 16) | 0; }
+
+pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                          const int32_t* q_start_loc, int32_t num_tokens,
+                          int64_t* slot_mapping, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (slot_mapping == nullptr) return fail(PA_ERR_INVALID_ARG, "slot_mapping is null");
+  if (seqs->num_seqs == 0) return fail(PA_ERR_INVALID_ARG, "tokens given but num_seqs is 0");
+  if (q_start_loc == nullptr && num_tokens != seqs->num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "without q_start_loc num_tokens (%d) must equal num_seqs (%d)",
+                num_tokens, seqs->num_seqs);
+  pa::SlotMappingArgs a{seqs->block_tables, seqs->context_lens, q_start_loc, slot_mapping,
+                        seqs->num_seqs, seqs->max_blocks_per_seq, num_tokens, pool->num_blocks};
+  return hip_status(pa::launch_slot_mapping(a, stream), "slot_mapping launch");
+}
+
+pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "k_new, v_new or slot_mapping is null");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  pa::WriteKVArgs a{k_new, v_new, pool->k_cache, pool->v_cache, slot_mapping, num_tokens,
+                    pool->num_kv_heads * pool->head_dim * elt_size(pool->dtype),
+                    static_cast<int64_t>(pool->num_blocks) * pool->block_size};
+  return hip_status(pa::launch_write_kv(a, stream), "write_kv launch");
+}
+
+size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t partition_size) {
+  if (seqs == nullptr || seqs->num_seqs < 0 || seqs->max_blocks_per_seq <= 0 ||
+      seqs->max_context_len < 0 || num_q_heads <= 0 || head_dim <= 0 ||
+      block_size != pa::kBlockSize || partition_size < 0 || partition_size % block_size != 0)
+    return 0;
+  return pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, seqs->max_context_len,
+                         num_q_heads, head_dim, partition_size)
+      .workspace_bytes;
+}
+
+pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q, void* out,
+                    int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_heads(pool, num_q_heads)) != PA_OK) return st;
+  if (partition_size < 0 || partition_size % pool->block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a multiple of block_size %d",
+                partition_size, pool->block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (seqs->num_seqs == 0) return PA_OK;
+  if (q == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "q or out is null");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  const pa::DecodePlan plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq,
+                                              seqs->max_context_len, num_q_heads,
+                                              pool->head_dim, partition_size);
+  if (plan.num_partitions > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%d partitions (at most 65535)", plan.num_partitions);
+  if (seqs->num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most 65535)", seqs->num_seqs);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                  plan.workspace_bytes, workspace == nullptr ? size_t(0) : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    part_o = static_cast<float*>(workspace);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
+  }
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.block_tables = seqs->block_tables;
+  a.context_lens = seqs->context_lens;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.num_seqs = seqs->num_seqs;
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = pool->head_dim;
+  a.dtype = pool->dtype;
+  a.max_blocks_per_seq = seqs->max_blocks_per_seq;
+  a.context_cap = plan.context_cap;
+  a.partition_size = plan.partition_size;
+  a.num_partitions = plan.num_partitions;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pa::launch_decode(a, stream), "decode launch");
+}
+
+pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q, void* out,
+                     const int32_t* q_start_loc, int32_t total_q_tokens, int32_t max_q_len,
+                     int32_t num_q_heads, float scale, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_heads(pool, num_q_heads)) != PA_OK) return st;
+  if (pool->dtype != PA_BF16 || pool->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 pools with head_dim 128");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (total_q_tokens < 0 || max_q_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "total_q_tokens %d / max_q_len %d < 0", total_q_tokens,
+                max_q_len);
+  if (seqs->num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (q == nullptr || out == nullptr || q_start_loc == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "q, out or q_start_loc is null");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  pa::PrefillArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.block_tables = seqs->block_tables;
+  a.context_lens = seqs->context_lens;
+  a.q_start_loc = q_start_loc;
+  a.num_seqs = seqs->num_seqs;
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = pool->head_dim;
+  a.max_blocks_per_seq = seqs->max_blocks_per_seq;
+  a.context_cap = context_cap(seqs);
+  a.max_q_len = max_q_len;
+  a.total_q_tokens = total_q_tokens;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pa::launch_prefill(a, stream), "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal interface between the C-ABI entry points (pa_api.cpp) and the
+// kernel launchers.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kBlockSize = 16;  // tokens per physical block the kernels handle
+
+struct SlotMappingArgs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* q_start_loc;  // may be null (one token per sequence)
+  int64_t* slot_mapping;
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t num_tokens;
+  int32_t num_blocks;
+};
+hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t stream);
+
+struct WriteKVArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_bytes;       // num_kv_heads * head_dim * element size (multiple of 16)
+  int64_t num_slots;       // num_blocks * block_size
+};
+hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_o;           // [num_seqs, num_q_heads, num_partitions, head_dim]
+  float* part_ml;          // [num_seqs, num_q_heads, num_partitions, 2]
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t dtype;           // 0 = f32, 1 = bf16
+  int32_t max_blocks_per_seq;
+  int32_t context_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
+  int32_t partition_size;  // tokens per partition, multiple of the block size
+  int32_t num_partitions;  // ceil(context_cap / partition_size), >= 1
+  float scale_log2;        // softmax scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* q_start_loc;
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t context_cap;
+  int32_t max_q_len;
+  int32_t total_q_tokens;
+  float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Partition plan shared by the workspace query and pa_decode.
+struct DecodePlan {
+  int32_t context_cap;
+  int32_t partition_size;
+  int32_t num_partitions;
+  size_t workspace_bytes;
+  size_t part_ml_offset;   // byte offset of part_ml inside the workspace
+};
+DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       int32_t num_q_heads, int32_t head_dim, int32_t partition_size);
+
+}  // namespace pa

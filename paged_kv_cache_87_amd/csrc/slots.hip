@@ -1,0 +1,87 @@
+// Slot mapping and the slot-mapped K/V write (gfx950).
+//
+// A token at position `pos` of sequence `s` lives in logical block
+// pos / 16 at offset pos % 16; the block table maps the logical block to a
+// physical block, and the token's slot is the flat row
+// physical * 16 + offset of the pool viewed as [num_blocks * 16, Hkv, D]
+// (JuliaPagedAttn README, "Project Structure": slot mapping in the cache
+// layout; nanoserve Day 19, "Diagram": slot_mapping).  The write copies each
+// new token's [Hkv, D] row into its slot bit for bit (JuliaPagedAttn "API
+// Reference": write_kv_cache!; nanoserve Day 19 "What I added today").
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kSlotThreads = 256;
+constexpr int kWriteThreads = 256;
+
+__global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingArgs a) {
+  const int i = blockIdx.x * kSlotThreads + threadIdx.x;
+  if (i >= a.num_tokens) return;
+  int s, q_len, idx;
+  if (a.q_start_loc == nullptr) {
+    s = i;
+    q_len = 1;
+    idx = 0;
+  } else {
+    // Last sequence whose first token is <= i (empty sequences share their
+    // start with the next one, so the last such sequence is the owner).
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.q_start_loc[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    q_len = a.q_start_loc[s + 1] - a.q_start_loc[s];
+    idx = i - a.q_start_loc[s];
+  }
+  const int L = a.context_lens[s];
+  const int pos = L - q_len + idx;
+  int64_t slot = -1;
+  if (idx >= 0 && idx < q_len && pos >= 0 && pos < L) {
+    const int logical = pos / kBlockSize;
+    if (logical < a.max_blocks_per_seq) {
+      const int phys = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + logical];
+      if (phys >= 0 && phys < a.num_blocks)
+        slot = static_cast<int64_t>(phys) * kBlockSize + (pos % kBlockSize);
+    }
+  }
+  a.slot_mapping[i] = slot;
+}
+
+// One 16-byte chunk per thread; blockIdx.y selects K (0) or V (1).
+__global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) {
+  const int chunks_per_row = a.row_bytes >> 4;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * chunks_per_row;
+  if (c >= total) return;
+  const int t = static_cast<int>(c / chunks_per_row);
+  const int part = static_cast<int>(c - static_cast<int64_t>(t) * chunks_per_row);
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
+  uint4* dst = static_cast<uint4*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  dst[slot * chunks_per_row + part] = src[static_cast<int64_t>(t) * chunks_per_row + part];
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t stream) {
+  const int grid = (a.num_tokens + kSlotThreads - 1) / kSlotThreads;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(kSlotThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * (a.row_bytes >> 4);
+  const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
+  hipLaunchKernelGGL(write_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

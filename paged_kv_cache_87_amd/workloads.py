@@ -15,6 +15,7 @@ no sequence owns, so a read past a sequence's last block lands on poison.
 
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -34,11 +35,40 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     import torch
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def normal_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
+_CHUNK = 1 << 22
+
+
+def _fill_normal(out: np.ndarray, seed: int, tag: int) -> None:
+    """N(0,1) float32 draws into ``out`` (1-D), chunk c drawn from its own
+    PCG64 stream keyed by (seed, tag, c): the result does not depend on how
+    many threads fill it."""
+    n = out.shape[0]
+
+    def one(c):
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(tag, c))
+        g = np.random.Generator(np.random.PCG64(ss))
+        a = c * _CHUNK
+        g.standard_normal(size=min(_CHUNK, n - a), dtype=np.float32, out=out[a:a + _CHUNK])
+
+    chunks = range((n + _CHUNK - 1) // _CHUNK)
+    if n <= _CHUNK:
+        for c in chunks:
+            one(c)
+        return
+    import concurrent.futures as cf
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, chunks))
+
+
+def normal_values(seed: int, tag: int, shape, dtype: str) -> np.ndarray:
+    """N(0,1) values of ``shape``: float32, or bf16 bit patterns (RNE)."""
+    x = np.empty(int(np.prod(shape)), dtype=np.float32)
+    _fill_normal(x, seed, tag)
+    x = x.reshape(shape)
     if dtype == F32:
         return x
     if dtype == BF16:
@@ -110,7 +140,9 @@ class Workload:
     def empty_pool(self) -> np.ndarray:
         shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
         fill = poison_value(self.dtype) if self.pool_fill == "nan" else 0
-        return np.full(shape, fill, dtype=storage_np_dtype(self.dtype))
+        pool = np.empty(shape, dtype=storage_np_dtype(self.dtype))
+        pool.fill(fill)
+        return pool
 
     def kv_bytes_read(self) -> int:
         """K and V bytes that one pass over every context reads."""
@@ -144,12 +176,13 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def _drawer(rng, dtype, with_values):
-    """Value source: N(0,1) draws, or (``with_values=False``, for checks of
-    the tables alone) zero-stride placeholders of the right shape that cost
-    no memory."""
+def _drawer(seed, dtype, with_values):
+    """Value source: successive N(0,1) arrays (tags 1, 2, ...), or (with
+    ``with_values=False``, for checks of the tables alone) zero-stride
+    placeholders of the right shape that cost no memory."""
     if with_values:
-        return lambda shape: normal_values(rng, shape, dtype)
+        tags = iter(range(1, 1 << 30))
+        return lambda shape: normal_values(seed, next(tags), shape, dtype)
     z = np.zeros((), dtype=storage_np_dtype(dtype))
     return lambda shape: np.broadcast_to(z, shape)
 
@@ -182,7 +215,7 @@ def decode_workload(name, seed, *, dtype, num_q_heads, num_kv_heads, head_dim,
     hist_start = np.minimum(hist_start, hist_end)
     n_hist = int((hist_end - hist_start).astype(np.int64).sum())
     Hkv, D = num_kv_heads, head_dim
-    draw = _drawer(rng, dtype, with_values)
+    draw = _drawer(seed, dtype, with_values)
     hist_k = draw((n_hist, Hkv, D))
     hist_v = draw((n_hist, Hkv, D))
     new_k = draw((S, Hkv, D))
@@ -218,7 +251,7 @@ def prefill_workload(name, seed, *, dtype, num_q_heads, num_kv_heads, head_dim,
     n_hist = int(hist_end.astype(np.int64).sum())
     T = int(q_lens.astype(np.int64).sum())
     Hkv, D = num_kv_heads, head_dim
-    draw = _drawer(rng, dtype, with_values)
+    draw = _drawer(seed, dtype, with_values)
     hist_k = draw((n_hist, Hkv, D))
     hist_v = draw((n_hist, Hkv, D))
     new_k = draw((T, Hkv, D))
