@@ -1,0 +1,220 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+Workload: Llama-style GQA decode -- batch 64, 32 query / 8 KV heads,
+head_dim 128, bf16 K/V, block size 16, contexts uniform in [1, 8192] (seeded),
+random block tables over a 40000-block pool.  One step is the whole hot path
+for one new token per sequence: slot mapping, the K/V write of the new
+token, the partitioned decode kernel and the log-sum-exp merge, all through
+libpa.so on torch's current stream, with every input already resident in
+HBM.
+
+Printed: one JSON line with whole-step throughput (KV bytes read per second),
+the decode call's roofline (KV bytes / decode+merge time against 8 TB/s,
+timed with events over the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged-attn decode μs/step + KV-read HBM GB/s (% of peak), batch 64 ctx 4096"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="wall-time budget of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--fixed-context", type=int, default=None,
+                   help="every context at this length instead of uniform [1, 8192]")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "pa_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_87_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str, partition_size: int):
+    """HBM bytes per decode call from committed rocprofv3 counter runs, if
+    they were taken on the current decode source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    if rec.get("workload") != workload_name or rec.get("partition_size") != partition_size:
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands on the host: pools built and the step's write
+    done untimed, then decode of whole sequences, in order, until the time
+    budget is used up."""
+    import numpy as np
+
+    from oracle import run as orun
+    import oracle.paged_attention as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl absent or unreadable
+        blas_threads = 1
+    k_cache, v_cache = orun.build_pools(w)
+    orun.write_step(w, k_cache, v_cache)
+    done, kv_bytes = 0, 0
+    elt = 2 if w.dtype == "bf16" else 4
+    t0 = time.perf_counter()
+    for s in range(w.num_seqs):
+        orc.decode(w.q[s:s + 1], k_cache, v_cache, w.block_tables[s:s + 1],
+                   w.context_lens[s:s + 1], w.scale, w.dtype)
+        done += 1
+        kv_bytes += 2 * w.num_kv_heads * w.head_dim * elt * int(w.context_lens[s])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": kv_bytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"decode of the first {done} of {w.num_seqs} sequences "
+                  f"({int(np.sum(w.context_lens[:done]))} context tokens, {kv_bytes / 1e9:.3f} GB of K/V) "
+                  f"in {dt:.1f} s, numpy float64; host CPU {model!r}, "
+                  f"{len(os.sched_getaffinity(0))} cores visible",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange; "
+              "this build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_87_amd import binding, runner
+    from paged_kv_cache_87_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load_library()
+    torch.cuda.set_device(0)
+
+    w = wl.llama_gqa_decode(pool_fill="zero", partition_size=args.partition_size,
+                            fixed_context=args.fixed_context)
+    g = runner.GpuStep(w)
+    g.write_history()
+    kv_bytes = w.kv_bytes_read()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        g.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        g.slot_mapping()
+        g.write()
+        ev[i][0].record(stream)
+        g.attend()
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    step_ms = total_ms / K
+    dec_avg_ms = float(np.mean(decode_ms))
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+
+    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
+
+    traffic = measured_traffic(w.name, args.partition_size)
+    rec = {
+        "metric": METRIC,
+        "value": kv_bytes / (step_ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "us_per_step": step_ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.num_seqs,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "context_lens": ("fixed %d" % args.fixed_context) if args.fixed_context
+            else "uniform [1, 8192], seed 87003",
+            "sum_context_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "kv_bytes_per_step": kv_bytes,
+            "partition_size": args.partition_size,
+        },
+        "decode_us": {"mean": dec_avg_ms * 1e3, "p10": float(np.percentile(decode_ms, 10)) * 1e3,
+                      "p50": float(np.percentile(decode_ms, 50)) * 1e3,
+                      "p90": float(np.percentile(decode_ms, 90)) * 1e3},
+        "roofline": {
+            "kernel": "pa_decode (partition kernel + log-sum-exp merge)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,7 +174,7 @@ size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads,
  * pa_decode_workspace_bytes(...)) holds the per-partition results; its
  * contents on entry do not matter.
  *
- * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}; num_seqs <= 4096.
  */
 pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
                     void* out, int32_t num_q_heads, float scale, int32_t partition_size,

@@ -48,6 +48,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegBig = -1.0e30f;  // "no score yet": finite, so m - m stays 0
+constexpr int kChunkBlocks = 64 * kWaves;  // blocks whose table entries one load brings in
+constexpr int kRing = 2;                    // blocks per wave in the load ring
+constexpr float kRescaleLog2 = 8.f;         // reference-max slack before a rescale
 
 // Head index, relative to the lane's own head, held at position idx of the
 // reduce-scatter input when the group has 2^R heads.  Level k of the scatter
@@ -157,6 +160,25 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   else static_cast<float*>(out)[idx] = v;
 }
 
+// Persistent driver.  Each workgroup first builds, in LDS, the list of work
+// units of the whole batch: unit = (sequence, partition, KV head), full
+// partitions first and each sequence's partial last partition after them (so
+// the short units fill the tail), KV head fastest (the heads of one partition
+// read the same physical blocks at about the same time).  It then takes
+// units blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized to what
+// the GPU holds at once, so no workgroup is launched only to find no work.
+//
+// Inside a unit the four waves take the partition's blocks round-robin, each
+// through a ring of kRing register buffers (kRing-1 blocks in flight while
+// one is computed).  Between units nothing drains: while unit u computes, the
+// table entries of unit u+1 are already loaded, and the query rows and first
+// ring blocks of unit u+1 are issued right after unit u's output stores, so
+// the memory pipe stays busy across unit boundaries.  Every wait the
+// compiler places inside the ring is then exact, because whatever reaches
+// the ring's loop header has the two primed blocks as its youngest loads.
+//
+// Plan in dynamic LDS: ctx[S] clamped context lengths, pre_full[S+1] and
+// pre_part[S+1] exclusive prefix sums of the full / partial partition counts.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   using LT = Layout<T, D>;
@@ -166,45 +188,159 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int NW = LT::kNW;
   using F = Frag<NW>;
 
+  extern __shared__ int32_t sm_plan[];
+  __shared__ int32_t sm_scan[2][kThreads];
   __shared__ float sm_acc[kWaves][N][D];
   __shared__ float sm_m[kWaves][N];
   __shared__ float sm_l[kWaves][N];
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
+  const int S = a.num_seqs;
+  const int P = a.partition_size;
+  int32_t* const sm_ctx = sm_plan;
+  int32_t* const sm_pf = sm_plan + S;
+  int32_t* const sm_pp = sm_pf + S + 1;
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int row = lane >> 4;
   const int li = lane & 15;
 
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
-  const int P = a.partition_size;
-  const int npart = L > 0 ? (L + P - 1) / P : 1;
-  if (part >= npart) return;
-  const int tok0 = part * P;
-  const int tok1 = (tok0 + P < L) ? tok0 + P : L;
-  const int blk0 = tok0 / kBlockSize;
-  const int blk1 = (tok1 + kBlockSize - 1) / kBlockSize;
-
-  // ---- query heads of the group, in this lane's scatter order -------------
-  const int own = li >> (4 - R);     // head whose full score this lane ends with
-  uint32_t qv[N][NW];
+  // ---- the plan --------------------------------------------------------------
   {
+    const int per = (S + kThreads - 1) / kThreads;   // run of sequences per thread
+    const int b0 = min(S, tid * per);
+    const int b1 = min(S, b0 + per);
+    int cf = 0, cp = 0;
+    for (int q = b0; q < b1; ++q) {
+      int L = a.context_lens[q];
+      L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
+      sm_ctx[q] = L;
+      cf += L / P;
+      cp += (L % P != 0 || L == 0) ? 1 : 0;
+    }
+    sm_scan[0][tid] = cf;
+    sm_scan[1][tid] = cp;
+    __syncthreads();
+    if (tid < 64) {
+      // exclusive scan of the 256 per-thread counts: 4 per lane, then the wave
+      int f[4], pp[4], tf = 0, tp = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = sm_scan[0][4 * tid + i];
+        pp[i] = sm_scan[1][4 * tid + i];
+        tf += f[i];
+        tp += pp[i];
+      }
+      int xf = tf, xp = tp;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int yf = __shfl_up(xf, off);
+        const int yp = __shfl_up(xp, off);
+        if (tid >= off) { xf += yf; xp += yp; }
+      }
+      int ef = xf - tf, ep = xp - tp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm_scan[0][4 * tid + i] = ef;
+        sm_scan[1][4 * tid + i] = ep;
+        ef += f[i];
+        ep += pp[i];
+      }
+      if (tid == 63) {
+        sm_pf[S] = xf;
+        sm_pp[S] = xp;
+      }
+    }
+    __syncthreads();
+    int ef = sm_scan[0][tid], ep = sm_scan[1][tid];
+    for (int q = b0; q < b1; ++q) {
+      const int L = sm_ctx[q];
+      sm_pf[q] = ef;
+      sm_pp[q] = ep;
+      ef += L / P;
+      ep += (L % P != 0 || L == 0) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  const int n_full = sm_pf[S];
+  const int n_units = (n_full + sm_pp[S]) * a.num_kv_heads;
+
+  // ---- unit description --------------------------------------------------------
+  struct Unit {
+    int s, part, g, L, tok1, blk0, blk1, npart;
+  };
+  // last sequence q with pre[q] <= r (runs of equal prefixes end at the
+  // sequence that owns the unit)
+  auto owner = [&](const int32_t* pre, int r) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto unit_at = [&](int u) {
+    Unit x;
+    x.g = u % a.num_kv_heads;
+    const int r = u / a.num_kv_heads;
+    if (r < n_full) {
+      x.s = owner(sm_pf, r);
+      x.part = r - sm_pf[x.s];
+    } else {
+      x.s = owner(sm_pp, r - n_full);
+      x.part = sm_ctx[x.s] / P;
+    }
+    x.L = sm_ctx[x.s];
+    x.npart = x.L > 0 ? (x.L + P - 1) / P : 1;
+    const int tok0 = x.part * P;
+    x.tok1 = (tok0 + P < x.L) ? tok0 + P : x.L;
+    x.blk0 = tok0 / kBlockSize;
+    x.blk1 = (x.tok1 + kBlockSize - 1) / kBlockSize;
+    return x;
+  };
+  // lane t: table entry of this wave's t-th block of the chunk at c0
+  auto load_tbl = [&](const Unit& x, int c0) {
+    const int j = c0 + wave + kWaves * lane;
+    const int lim = min(x.blk0 + P / kBlockSize, a.max_blocks_per_seq);
+    return j < lim ? a.block_tables[static_cast<int64_t>(x.s) * a.max_blocks_per_seq + j] : -1;
+  };
+  const int own = li >> (4 - R);     // head whose full score this lane ends with
+  // query rows of the unit's heads, in this lane's scatter order
+  auto load_q = [&](const Unit& x, uint32_t (&qd)[N][NW]) {
     const char* qb = static_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(s) * a.num_q_heads + g * N) * D + li * EPL) * LT::kElt;
+                     ((static_cast<int64_t>(x.s) * a.num_q_heads + x.g * N) * D + li * EPL) * LT::kElt;
 #pragma unroll
     for (int idx = 0; idx < N; ++idx) {
       const int h = own ^ scatter_head_xor<R>(idx);
       const F f = load_frag<NW>(qb + static_cast<int64_t>(h) * D * LT::kElt);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) qv[idx][w] = f.w[w];
+      for (int w = 0; w < NW; ++w) qd[idx][w] = f.w[w];
     }
-  }
+  };
+
   int slot_head[N];                  // head carried by accumulator slot j
   bcast_all_i<R>(own, slot_head);
+
+  const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * LT::kElt;
+  const uint32_t block_bytes = row_bytes * kBlockSize;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  const float sl2 = a.scale_log2;
+
+  // ---- current unit state -------------------------------------------------------
+  int u = blockIdx.x;
+  if (u >= n_units) return;
+  Unit cur = unit_at(u);
+  int c0 = cur.blk0;                 // first block of the current chunk
+  int nk = 0;                        // this wave's blocks in the current chunk
+  int tbl = load_tbl(cur, c0);
+  uint32_t qv[N][NW];
+  load_q(cur, qv);
+  uint32_t lane_off = (cur.g * D + li * EPL) * LT::kElt + row * row_bytes;
+  auto chunk_blocks = [&](const Unit& x, int cs) {
+    const int ce = min(x.blk1, cs + kChunkBlocks);
+    return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
+  };
 
   float m = kNegBig, l = 0.f;
   float acc[N][EPL];
@@ -213,198 +349,331 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
 
-  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * LT::kElt;
-  const int64_t block_bytes = row_bytes * kBlockSize;
-  const int64_t lane_off = (static_cast<int64_t>(g) * D + li * EPL) * LT::kElt + row * row_bytes;
-  const char* kbase = static_cast<const char*>(a.k_cache) + lane_off;
-  const char* vbase = static_cast<const char*>(a.v_cache) + lane_off;
-  const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const float sl2 = a.scale_log2;
-
-  // Valid tokens of block j (0 when its table entry is not a pool block).
-  auto block_valid = [&](int j, int& phys) {
-    phys = uniform(table[j]);
-    const bool bad = phys < 0 || phys >= a.num_blocks;
-    if (bad) phys = 0;
-    const int n = tok1 - j * kBlockSize;
-    return bad ? 0 : (n < kBlockSize ? n : kBlockSize);
-  };
-
-  auto load_block = [&](int phys, F (&kf)[4], F (&vf)[4]) {
-    const int64_t off = static_cast<int64_t>(phys) * block_bytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      kf[u] = load_frag<NW>(kbase + off + u * 4 * row_bytes);
-      vf[u] = load_frag<NW>(vbase + off + u * 4 * row_bytes);
+  // Issue the loads of this wave's k-th block of the current chunk into
+  // (kf, vf) and return its number of valid tokens.  Past the wave's last
+  // block, or for a table entry outside the pool, the descriptors have size
+  // 0: the loads return zeros without touching memory and the block counts 0
+  // valid tokens.
+  auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
+    int phys = -1;
+    int nvalid = 0;
+    if (k < nk) {
+      const int j = c0 + wave + kWaves * k;
+      phys = __builtin_amdgcn_readlane(tbl, k);
+      const int n = cur.tok1 - j * kBlockSize;
+      nvalid = n < kBlockSize ? n : kBlockSize;
     }
+    const bool ok = phys >= 0 && phys < a.num_blocks;
+    if (!ok) nvalid = 0;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * block_bytes : 0;
+    const Rsrc rk = make_rsrc(kpool + off, ok ? block_bytes : 0u);
+    const Rsrc rv = make_rsrc(vpool + off, ok ? block_bytes : 0u);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) kf[uu] = load_frag_buf<NW>(rk, lane_off + uu * 4 * row_bytes);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) vf[uu] = load_frag_buf<NW>(rv, lane_off + uu * 4 * row_bytes);
+    return nvalid;
   };
 
+  // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
+  // running max and sum, then P.V.  The reference max of a stream only moves
+  // when a score passes it by more than kRescaleLog2 (then the accumulators
+  // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
+  // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
   auto process = [&](F (&kf)[4], F (&vf)[4], int nvalid) {
     float z[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int uu = 0; uu < 4; ++uu) {
       float part_dot[N];
 #pragma unroll
-      for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[u], 0.f);
-      z[u] = reduce_scatter<R>(part_dot) * sl2;
+      for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
+      z[uu] = reduce_scatter<R>(part_dot) * sl2;
     }
+    // tokens past the context (partial last block, or a block the ring runs
+    // past its end) get no weight and a zero value row, whatever the pool
+    // holds there
     if (nvalid < kBlockSize) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (row + 4 * u >= nvalid) {
-          z[u] = -INFINITY;
+      for (int uu = 0; uu < 4; ++uu) {
+        if (row + 4 * uu >= nvalid) {
+          z[uu] = -INFINITY;
 #pragma unroll
-          for (int w = 0; w < NW; ++w) vf[u].w[w] = 0u;
+          for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
         }
       }
     }
     const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
+      const float m_new = mx > m + kRescaleLog2 ? mx : m;
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+      float alpha_j[N];
+      bcast_all<R>(alpha, alpha_j);
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
+    }
     float p[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) p[u] = fast_exp2(z[u] - m_new);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = m_new;
+    for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
 
-    float alpha_j[N];
-    bcast_all<R>(alpha, alpha_j);
+    if constexpr (sizeof(T) == 2) {
+      // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
+      // with one v_dot2_f32_bf16 per (head, element): the value rows of the
+      // pair are interleaved with v_perm, the weights packed to bf16.
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int j = 0; j < N; ++j)
+      for (int pr = 0; pr < 2; ++pr) {
+        const int ua = 2 * pr, ub = 2 * pr + 1;
+        float pa[N], pb[N];
+        bcast_all<R>(p[ua], pa);
+        bcast_all<R>(p[ub], pb);
+        uint32_t pw[N];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
+        for (int j = 0; j < N; ++j) {
+          const f32x2 two = {pa[j], pb[j]};
+          pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+        }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float pj[N];
-      bcast_all<R>(p[u], pj);
+        for (int w = 0; w < NW; ++w) {
+          // element 2w: low halves of token a and b; element 2w+1: high halves
+          const uint32_t ve = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x05040100u);
+          const uint32_t vo = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x07060302u);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float v = frag_elem<T, D>(vf[u], e);
+          for (int j = 0; j < N; ++j) {
+            acc[j][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, ve), acc[j][2 * w],
+                false);
+            acc[j][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, vo),
+                acc[j][2 * w + 1], false);
+          }
+        }
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
+      for (int uu = 0; uu < 4; ++uu) {
+        float pj[N];
+        bcast_all<R>(p[uu], pj);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float v = frag_elem<T, D>(vf[uu], e);
+#pragma unroll
+          for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
+        }
       }
     }
   };
 
-  // ---- main loop: blocks blk0+wave, +4, ... with one block prefetched -----
-  {
-    F ka[4], va[4], kb[4], vb[4];
-    int j = blk0 + wave;
-    int phys_a = 0, phys_b = 0, nva = 0, nvb = 0;
-    if (j < blk1) {
-      nva = block_valid(j, phys_a);
-      load_block(phys_a, ka, va);
-    }
-    while (j < blk1) {
-      if (j + kWaves < blk1) {
-        nvb = block_valid(j + kWaves, phys_b);
-        load_block(phys_b, kb, vb);
-      }
-      process(ka, va, nva);
-      j += kWaves;
-      if (j >= blk1) break;
-      if (j + kWaves < blk1) {
-        nva = block_valid(j + kWaves, phys_a);
-        load_block(phys_a, ka, va);
-      }
-      process(kb, vb, nvb);
-      j += kWaves;
-    }
-  }
+  // ---- prologue: the first unit's table and query rows, then the next unit's
+  // (left in flight), then the first unit's primed ring blocks -----------------
+  __builtin_amdgcn_s_waitcnt(0);
+  int un = u + gridDim.x;
+  bool has_next = un < n_units;
+  Unit nxt = has_next ? unit_at(un) : cur;
+  int tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
+  nk = chunk_blocks(cur, c0);
 
-  // ---- merge the four rows of the wave -------------------------------------
-  float ms[N], ls[N];
-  bcast_all<R>(m, ms);
-  bcast_all<R>(l, ls);
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const float mo = __shfl_xor(ms[j], off);
-      const float lo = __shfl_xor(ls[j], off);
-      const float mn = fmaxf(ms[j], mo);
-      const float c0 = fast_exp2(ms[j] - mn);
-      const float c1 = fast_exp2(mo - mn);
-      ls[j] = ls[j] * c0 + lo * c1;
-      ms[j] = mn;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = acc[j][e] * c0 + __shfl_xor(acc[j][e], off) * c1;
-    }
-  }
+  F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+  int n0 = issue(0, k0, v0);
+  __builtin_amdgcn_sched_barrier(0);
+  int n1 = 0;
+  if constexpr (kRing == 3) n1 = issue(1, k1, v1);
+  __builtin_amdgcn_sched_barrier(0);
+  int n2 = 0;
 
-  // ---- merge the waves through LDS -----------------------------------------
-  if (row == 0) {
+  for (;;) {
+    // ---- the ring over this chunk of the current unit (one exit, at the
+    // bottom: a trip always runs every stage; stages past the wave's last
+    // block see size-0 descriptors and zero valid tokens and change nothing)
+    if constexpr (kRing == 2) {
+      for (int k = 0; k < nk; k += 2) {
+        n1 = issue(k + 1, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k0, v0, n0);
+        n0 = issue(k + 2, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k1, v1, n1);
+      }
+    } else {
+      for (int k = 0; k < nk; k += 3) {
+        n2 = issue(k + 2, k2, v2);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k0, v0, n0);
+        n0 = issue(k + 3, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k1, v1, n1);
+        n1 = issue(k + 4, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k2, v2, n2);
+      }
+    }
+
+    // ---- a partition longer than one chunk: next chunk of the same unit ------
+    if (c0 + kChunkBlocks < cur.blk1) {
+      c0 += kChunkBlocks;
+      tbl = load_tbl(cur, c0);
+      __builtin_amdgcn_s_waitcnt(0);
+      nk = chunk_blocks(cur, c0);
+      n0 = issue(0, k0, v0);
+      __builtin_amdgcn_sched_barrier(0);
+      n1 = issue(1, k1, v1);
+      __builtin_amdgcn_sched_barrier(0);
+      continue;
+    }
+
+    // ---- merge the four rows of each wave -------------------------------------
+    {
+      float ms[N], ls[N];
+      bcast_all<R>(m, ms);
+      bcast_all<R>(l, ls);
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          const float mo = __shfl_xor(ms[j], off);
+          const float lo = __shfl_xor(ls[j], off);
+          const float mn = fmaxf(ms[j], mo);
+          const float ca = fast_exp2(ms[j] - mn);
+          const float cb = fast_exp2(mo - mn);
+          ls[j] = ls[j] * ca + lo * cb;
+          ms[j] = mn;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[j][e] = acc[j][e] * ca + __shfl_xor(acc[j][e], off) * cb;
+        }
+      }
+      // ---- merge the waves through LDS ------------------------------------------
+      if (row == 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
+        if ((li & (W - 1)) == 0) {
+          sm_m[wave][own] = ms[0];
+          sm_l[wave][own] = ls[0];
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const bool direct = cur.npart == 1;
+      for (int o = tid; o < N * D; o += kThreads) {
+        const int h = o / D;
+        const int d = o - h * D;
+        float M = sm_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float c = fast_exp2(sm_m[w][h] - M);
+          lsum += sm_l[w][h] * c;
+          osum += sm_acc[w][h][d] * c;
+        }
+        const float val = lsum > 0.f ? osum / lsum : 0.f;
+        const int qh = cur.g * N + h;
+        if (direct) {
+          store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
+        } else {
+          const int64_t pi =
+              (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * a.num_partitions + cur.part;
+          a.part_o[pi * D + d] = val;
+          if (d == 0) {
+            a.part_ml[pi * 2 + 0] = M;
+            a.part_ml[pi * 2 + 1] = lsum;
+          }
+        }
+      }
+    }
+    __syncthreads();   // LDS merge buffers are reused by the next unit
+    if (!has_next) break;
+
+    // ---- move on: loads of the unit after next, then the next unit's primed
+    // ring blocks (in that order, so the primed blocks are the youngest loads)
+    cur = nxt;
+    u = un;
+    un = u + gridDim.x;
+    has_next = un < n_units;
+    if (has_next) nxt = unit_at(un);
+    tbl = tbl_nxt;
+    load_q(cur, qv);
+    tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
+    c0 = cur.blk0;
+    nk = chunk_blocks(cur, c0);
+    lane_off = (cur.g * D + li * EPL) * LT::kElt + row * row_bytes;
+    m = kNegBig;
+    l = 0.f;
 #pragma unroll
     for (int j = 0; j < N; ++j)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
-    if ((li & (W - 1)) == 0) {
-      sm_m[wave][own] = ms[0];
-      sm_l[wave][own] = ls[0];
-    }
-  }
-  __syncthreads();
-
-  const bool direct = npart == 1;
-  for (int o = tid; o < N * D; o += kThreads) {
-    const int h = o / D;
-    const int d = o - h * D;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float c = fast_exp2(sm_m[w][h] - M);
-      lsum += sm_l[w][h] * c;
-      osum += sm_acc[w][h][d] * c;
-    }
-    const float val = lsum > 0.f ? osum / lsum : 0.f;
-    const int qh = g * N + h;
-    if (direct) {
-      store_out<T>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + qh) * D + d, val);
-    } else {
-      const int64_t pi = (static_cast<int64_t>(s) * a.num_q_heads + qh) * a.num_partitions + part;
-      a.part_o[pi * D + d] = val;
-      if (d == 0) {
-        a.part_ml[pi * 2 + 0] = M;
-        a.part_ml[pi * 2 + 1] = lsum;
-      }
-    }
+      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+    n0 = issue(0, k0, v0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kRing == 3) n1 = issue(1, k1, v1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
 // out = sum_j w_j o_j / sum_j w_j with w_j = l_j * 2^(m_j - max m).
+// One wave per row; the partition maxima are read lane-parallel, then every
+// lane accumulates D/64 output elements over the partitions.
+constexpr int kMergeThreads = 64;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  constexpr int E = D / kMergeThreads;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   int L = a.context_lens[s];
   L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
   const int npart = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 1;
   if (npart <= 1) return;  // the decode kernel wrote this row itself
   const int64_t base = (static_cast<int64_t>(s) * a.num_q_heads + h) * a.num_partitions;
+  const float* ml = a.part_ml + base * 2;
+  const float* po = a.part_o + base * D;
   float M = kNegBig;
-  for (int j = 0; j < npart; ++j) M = fmaxf(M, a.part_ml[(base + j) * 2]);
-  float wsum = 0.f, osum = 0.f;
+  for (int j = lane; j < npart; j += kMergeThreads) M = fmaxf(M, ml[2 * j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float wsum = 0.f;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+#pragma unroll 4
   for (int j = 0; j < npart; ++j) {
-    const float w = a.part_ml[(base + j) * 2 + 1] * fast_exp2(a.part_ml[(base + j) * 2] - M);
+    const float w = ml[2 * j + 1] * fast_exp2(ml[2 * j] - M);
     wsum += w;
-    osum += w * a.part_o[(base + j) * D + d];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[static_cast<int64_t>(j) * D + lane + e * kMergeThreads], o[e]);
   }
-  store_out<T>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + h) * D + d,
-               wsum > 0.f ? osum / wsum : 0.f);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t out_base = (static_cast<int64_t>(s) * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) store_out<T>(a.out, out_base + lane + e * kMergeThreads, o[e] * inv);
 }
 
 template <typename T, int D, int R>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<T, D, R>), grid, dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  const size_t lds = plan_lds_bytes(a.num_seqs);
+  const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R>);
+  int resident = 0;
+  hipError_t e = resident_workgroups(fn, kThreads, lds, &resident);
+  if (e != hipSuccess) return e;
+  const int64_t max_units =
+      static_cast<int64_t>(a.num_partitions) * a.num_kv_heads * a.num_seqs;
+  const int grid = static_cast<int>(resident < max_units ? resident : max_units);
+  hipLaunchKernelGGL((decode_kernel<T, D, R>), dim3(grid), dim3(kThreads), lds, stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

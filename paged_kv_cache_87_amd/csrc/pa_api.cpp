@@ -8,8 +8,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.h"
 
 namespace {
@@ -90,6 +93,35 @@ int32_t context_cap(const pa_seq_desc* seqs) {
 }  // namespace
 
 namespace pa {
+
+hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, size_t>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_tuple(fn, dev, lds);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int n = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = n;
+  }
+  *out = n;
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
                        int32_t num_q_heads, int32_t head_dim, int32_t partition_size) {
@@ -201,8 +233,9 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
                                               pool->head_dim, partition_size);
   if (plan.num_partitions > 65535)
     return fail(PA_ERR_UNSUPPORTED, "%d partitions (at most 65535)", plan.num_partitions);
-  if (seqs->num_seqs > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most 65535)", seqs->num_seqs);
+  if (seqs->num_seqs > pa::kMaxDecodeSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most %d)", seqs->num_seqs,
+                pa::kMaxDecodeSeqs);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (plan.workspace_bytes > 0) {

@@ -78,6 +78,18 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Decode work plan kept in LDS by every workgroup: clamped context lengths and
+// two prefix-sum arrays over the batch.
+constexpr int kMaxDecodeSeqs = 4096;
+inline size_t plan_lds_bytes(int num_seqs) {
+  return (3 * static_cast<size_t>(num_seqs) + 2) * sizeof(int32_t);
+}
+
+// Workgroups of kernel `fn` (block size `threads`, `lds` bytes of dynamic
+// LDS) that the current device holds at once; cached per (kernel, device,
+// LDS size).
+hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out);
+
 // Partition plan shared by the workspace query and pa_decode.
 struct DecodePlan {
   int32_t context_cap;
