@@ -1,9 +1,284 @@
-// Batched causal prefill (gfx950).  The matrix-core kernel is not in this
-// build yet; the launcher reports the call as unsupported.
+// Batched causal prefill for gfx950 on bf16 matrix cores: every new token of
+// every sequence attends to its paged history up to and including its own
+// position, all in one launch (JuliaPagedAttn README, "Features": batched
+// prefill, all prompt positions in a single kernel call; "Online Softmax").
+//
+// Work decomposition
+//   grid (query tile, kv_head, sequence), 256 threads = 4 waves.  A tile has
+//   128 columns = (query head of the GQA group, token) pairs: 128 / n_rep
+//   consecutive new tokens of the sequence times the n_rep query heads that
+//   share the KV head (GQA, nanoserve Day 19 "What I learned" item 4), so a
+//   K/V tile brought into LDS serves every head of the group.  Wave w owns
+//   columns 32w .. 32w+31.
+//   The keys are walked in tiles of 64 (four 16-token blocks, each found
+//   through the block table) up to the tile's last position; K is staged in
+//   LDS as [key][d], V transposed as [d][key], double-buffered.
+//
+// Arithmetic (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
+//   S^T = K . Q^T   : keys on the M axis, the wave's 32 columns on N; the
+//                     softmax reductions over keys are then mostly inside a
+//                     lane (16 keys per lane per 32-key tile) plus one swap
+//                     between the two lane halves.
+//   O^T += V^T . P^T: the accumulator layout of S^T, rounded to bf16, is
+//                     directly the B operand of the P.V product when the
+//                     contraction index k of lane half h is mapped to key
+//                     16c + 4h + (k mod 4) + 8 (k div 4) for 16-key step c;
+//                     the V^T fragments are read from LDS with the same map.
+//   Online softmax per column (running max / running sum); the reference max
+//   only moves when a score passes it by more than 2^8 (then O is rescaled).
+
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kD = 128;               // head_dim handled here
+constexpr int kCols = 128;            // (head, token) columns per workgroup
+constexpr int kKeys = 64;             // keys per K/V tile (4 blocks)
+constexpr int kKStride = kD + 8;      // LDS row stride of K (bf16 elements)
+constexpr int kVStride = kKeys + 8;   // LDS row stride of V^T (bf16 elements)
+constexpr float kPNegBig = -1.0e30f;
+constexpr float kPRescale = 8.f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct PrefillSmem {
+  uint16_t k[2][kKeys][kKStride];     // K tile, [key][d]
+  uint16_t vt[2][kD][kVStride];       // V tile transposed, [d][key]
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 two = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+}
+
+template <int R>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+  constexpr int NREP = 1 << R;
+  constexpr int TQ = kCols / NREP;    // tokens per tile
+  __shared__ PrefillSmem sm;
+
+  const int s = blockIdx.z;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;         // lane half: rows 4*half.. of each 8-row group
+  const int col = lane & 31;          // this lane's column inside the wave
+
+  const int qs0 = a.q_start_loc[s];
+  int q_len = a.q_start_loc[s + 1] - qs0;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
+  q_len = q_len < 0 ? 0 : (q_len > a.max_q_len ? a.max_q_len : q_len);
+  if (q_len > L) q_len = L;  // queries without a position in the context are skipped
+  const int n_tiles = (q_len + TQ - 1) / TQ;
+  // heaviest tiles (latest tokens, most keys) are launched first
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);
+  if (tile < 0) return;
+  const int t0 = tile * TQ;
+  const int first_pos = L - q_len;    // position of new token 0
+
+  // ---- this lane's column: (head, token) ----------------------------------
+  const int c = wave * 32 + col;
+  const int head = c / TQ;
+  const int tok = t0 + c % TQ;
+  const bool col_valid = tok < q_len;
+  const int qpos = first_pos + tok;   // the column's query position
+  const int qh = g * NREP + head;
+
+  // Q^T as B operand: lane holds q[d = 16*kk + 8*half + 0..7] for kk = 0..7
+  bf16x8 qf[kD / 16];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<int64_t>(qs0 + (col_valid ? tok : 0)) * a.num_q_heads + qh) * kD;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      uint4 x = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * half);
+      if (!col_valid) x = make_uint4(0u, 0u, 0u, 0u);
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // last key any column of the tile needs
+  const int last_tok = min(t0 + TQ, q_len) - 1;
+  const int key_end = first_pos + last_tok + 1;       // keys [0, key_end)
+  const int n_kt = (key_end + kKeys - 1) / kKeys;
+  const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * kD * 2;
+  const uint32_t block_bytes = row_bytes * kBlockSize;
+
+  // ---- K/V tile loader: 64 keys x 128 d, K as [key][d], V as [d][key] --------
+  // thread -> (key pair kp = tid / 16 * 2 .. +1, d chunk dc = tid % 16)
+  const int ld_key = (tid >> 4) * 2;  // 0, 2, ..., 30 (+32 for the second pass)
+  const int ld_dc = tid & 15;         // 8-element chunk of d
+  uint4 kreg[2][2], vreg[2][2];       // [pass][key of the pair]
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int key = ld_key + 32 * ps + e;
+        const int kpos = kt * kKeys + key;
+        uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
+        if (kpos < L) {
+          const int phys = table[kpos / kBlockSize];
+          if (phys >= 0 && phys < a.num_blocks) {
+            const int64_t off = static_cast<int64_t>(phys) * block_bytes +
+                                (kpos % kBlockSize) * row_bytes + (g * kD + ld_dc * 8) * 2;
+            kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_cache) + off);
+            vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_cache) + off);
+          }
+        }
+        kreg[ps][e] = kx;
+        vreg[ps][e] = vx;
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        *reinterpret_cast<uint4*>(&sm.k[buf][ld_key + 32 * ps + e][ld_dc * 8]) = kreg[ps][e];
+      // V^T: pair the two keys' values of each d into one dword
+      const uint32_t* va = reinterpret_cast<const uint32_t*>(&vreg[ps][0]);
+      const uint32_t* vb = reinterpret_cast<const uint32_t*>(&vreg[ps][1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = ld_dc * 8 + 2 * w;
+        const int key = ld_key + 32 * ps;
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d][key]) = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d + 1][key]) = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
+      }
+    }
+  };
+
+  f32x16 o[kD / 32];                  // O^T: 4 d-tiles of 32 x (32 columns)
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = kPNegBig, lsum = 0.f;
+  const float sl2 = a.scale_log2;
+
+  if (n_kt > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) fetch(kt + 1);   // next tile's loads fly during this tile's math
+
+    // ---- S^T = K . Q^T for the two 32-key halves of the tile ---------------
+    f32x16 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) {
+        const uint4 kx = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * t + col][16 * kk + 8 * half]);
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
+                                                         st[t], 0, 0, 0);
+      }
+    }
+    // ---- scale, causal mask, online softmax per column ---------------------
+    float tmax = kPNegBig;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt * kKeys + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float z = (col_valid && key <= qpos) ? st[t][r] * sl2 : -INFINITY;
+        st[t][r] = z;
+        tmax = fmaxf(tmax, z);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kPRescale) != 0) {
+      const float m_new = tmax > m + kPRescale ? tmax : m;
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    // P^T in bf16, packed straight from the accumulator layout
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(st[t][r] - m);
+        const float p1 = fast_exp2(st[t][r + 1] - m);
+        lsum += p0 + p1;
+        pk[t][r >> 1] = pack_bf16(p0, p1);
+      }
+    // ---- O^T += V^T . P^T over four 16-key steps -----------------------------
+#pragma unroll
+    for (int cstep = 0; cstep < kKeys / 16; ++cstep) {
+      const int t = cstep >> 1;
+      const int rb = (cstep & 1) * 4;   // dwords of pk[t] for this step
+      const uint4 pb = make_uint4(pk[t][rb], pk[t][rb + 1], pk[t][rb + 2], pk[t][rb + 3]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+      const int key_a = 16 * cstep + 4 * half;     // keys key_a..+3 and key_a+8..+11
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const int d = 32 * dt + col;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&sm.vt[buf][d][key_a]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&sm.vt[buf][d][key_a + 8]);
+        const uint4 vx = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf, o[dt],
+                                                         0, 0, 0);
+      }
+    }
+    // buffer buf^1 was last read in the previous tile, before its barrier
+    if (kt + 1 < n_kt) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds column `col`, rows d ----------------
+  lsum += __shfl_xor(lsum, 32);
+  if (!col_valid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                   (static_cast<int64_t>(qs0 + tok) * a.num_q_heads + qh) * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dt + 8 * r4 + 4 * half;
+      const uint2 w = make_uint2(pack_bf16(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
+                                 pack_bf16(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv));
+      *reinterpret_cast<uint2*>(orow + d) = w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const int n_rep = a.num_q_heads / a.num_kv_heads;
+  const int tq = kCols / n_rep;
+  const int tiles = (a.max_q_len + tq - 1) / tq;
+  dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
+  switch (n_rep) {
+    case 1: hipLaunchKernelGGL(prefill_kernel<0>, grid, dim3(kPThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(prefill_kernel<3>, grid, dim3(kPThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace pa
