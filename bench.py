@@ -1,19 +1,22 @@
-"""Paged-attention decode benchmark on one MI355X.
+"""Paged-attention benchmark on one MI355X.
 
-Workload: Llama-style GQA decode -- batch 64, 32 query / 8 KV heads,
-head_dim 128, bf16 K/V, block size 16, contexts uniform in [1, 8192] (seeded),
-random block tables over a 40000-block pool.  One step is the whole hot path
-for one new token per sequence: slot mapping, the K/V write of the new
-token, the partitioned decode kernel and the log-sum-exp merge, all through
-libpa.so on torch's current stream, with every input already resident in
-HBM.
+Headline workload: Llama-style GQA decode -- batch 64, 32 query / 8 KV heads,
+head_dim 128, bf16 K/V, block size 16, contexts uniform in [1, 8192]
+(seeded), random block tables over a 40000-block pool.  One step is the whole
+hot path for one new token per sequence: slot mapping, the K/V write of the
+new token, the partitioned decode kernel and the log-sum-exp merge, all
+through libpa.so on torch's current stream, with every input already
+resident in HBM.
 
-Printed: one JSON line with whole-step throughput (KV bytes read per second),
-the decode call's roofline (KV bytes / decode+merge time against 8 TB/s,
-timed with events over the timed region) and the CPU oracle timed on a
-bounded sample of the same workload.
+Printed: one JSON line with whole-step throughput (K/V bytes read per
+second), the decode call's roofline (K/V bytes / decode+merge time against
+8 TB/s, timed with events over the timed region), the CPU oracle timed on a
+bounded sample of the same workload, and secondary measurements of the
+batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16) and of the
+long-context shared-prefix decode.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+    python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 
 from __future__ import annotations
@@ -30,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode μs/step + KV-read HBM GB/s (% of peak), batch 64 ctx 4096"
 
 
@@ -38,12 +42,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--partition-size", type=int, default=512)
+    p.add_argument("--partition-size", type=int, default=1024)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="wall-time budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the prefill and long-context measurements")
     p.add_argument("--fixed-context", type=int, default=None,
                    help="every context at this length instead of uniform [1, 8192]")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain device copies of 1 GiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -73,10 +81,8 @@ def measured_traffic(workload_name: str, partition_size: int):
 
 def cpu_baseline(w, budget_s: float):
     """The oracle as it stands on the host: pools built and the step's write
-    done untimed, then decode of whole sequences, in order, until the time
-    budget is used up."""
-    import numpy as np
-
+    done untimed, then decode of whole sequences, in order (wrapping around),
+    until the time budget is used up."""
     from oracle import run as orun
     import oracle.paged_attention as orc
     try:
@@ -86,13 +92,15 @@ def cpu_baseline(w, budget_s: float):
         blas_threads = 1
     k_cache, v_cache = orun.build_pools(w)
     orun.write_step(w, k_cache, v_cache)
-    done, kv_bytes = 0, 0
+    done, kv_bytes, tokens = 0, 0, 0
     elt = 2 if w.dtype == "bf16" else 4
     t0 = time.perf_counter()
-    for s in range(w.num_seqs):
+    while True:
+        s = done % w.num_seqs
         orc.decode(w.q[s:s + 1], k_cache, v_cache, w.block_tables[s:s + 1],
                    w.context_lens[s:s + 1], w.scale, w.dtype)
         done += 1
+        tokens += int(w.context_lens[s])
         kv_bytes += 2 * w.num_kv_heads * w.head_dim * elt * int(w.context_lens[s])
         if time.perf_counter() - t0 > budget_s:
             break
@@ -111,12 +119,92 @@ def cpu_baseline(w, budget_s: float):
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"decode of the first {done} of {w.num_seqs} sequences "
-                  f"({int(np.sum(w.context_lens[:done]))} context tokens, {kv_bytes / 1e9:.3f} GB of K/V) "
-                  f"in {dt:.1f} s, numpy float64; host CPU {model!r}, "
-                  f"{len(os.sched_getaffinity(0))} cores visible",
+        "sample": f"{done} sequence decodes of this workload in order ({done / w.num_seqs:.2f} passes, "
+                  f"{tokens} context tokens, {kv_bytes / 1e9:.3f} GB of K/V) in {dt:.1f} s, numpy "
+                  f"float64; host CPU {model!r}, {len(os.sched_getaffinity(0))} cores visible",
         "seconds": dt,
     }
+
+
+def timed(torch, stream, K, W, prefix, body, suffix=None):
+    """Run W untimed then K timed iterations; each iteration is prefix(),
+    body() bracketed by events, suffix().  Returns (total ms / K, [body ms])."""
+    for _ in range(W):
+        prefix()
+        body()
+        if suffix:
+            suffix()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        prefix()
+        ev[i][0].record(stream)
+        body()
+        ev[i][1].record(stream)
+        if suffix:
+            suffix()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / K, [a.elapsed_time(b) for a, b in ev]
+
+
+def secondary(torch, np, stream, K, W):
+    from paged_kv_cache_87_amd import runner
+    from paged_kv_cache_87_amd import workloads as wl
+
+    out = {}
+    # batched causal prefill: slot mapping + write of every prompt token + prefill
+    w = wl.batched_prefill(pool_fill="zero")
+    g = runner.GpuStep(w)
+    g.write_history()
+    step_ms, pre_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend)
+    lens = w.context_lens.astype(np.int64)
+    flops = 2.0 * w.num_q_heads * w.head_dim * float(np.sum(lens * (lens + 1)))
+    pre = float(np.mean(pre_ms))
+    out["batched_prefill"] = {
+        "config": {"batch": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "prompt_lens": "uniform [256, 2048], seed 87004",
+                   "total_tokens": int(lens.sum())},
+        "us_per_step": step_ms * 1e3, "prefill_us": pre * 1e3,
+        "flops": flops, "tflops": flops / (pre * 1e-3) / 1e12,
+        "frac_bf16_peak": flops / (pre * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+    }
+    del g
+    torch.cuda.empty_cache()
+    # long-context decode over a copy-on-write shared prefix, partition 512
+    w = wl.long_context_cow(pool_fill="zero")
+    g = runner.GpuStep(w)
+    g.write_history()
+    step_ms, dec_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend)
+    dec = float(np.mean(dec_ms))
+    logical = w.kv_bytes_read()
+    prefix = w.meta["shared_prefix_tokens"]
+    unique = logical - (w.num_seqs - 1) * prefix * 2 * w.num_kv_heads * w.head_dim * 2
+    out["long_context_cow"] = {
+        "config": {"batch": w.num_seqs, "context": int(w.context_lens[0]), "shared_prefix": prefix,
+                   "partition_size": w.partition_size},
+        "us_per_step": step_ms * 1e3, "decode_us": dec * 1e3,
+        "logical_kv_GBps": logical / (dec * 1e-3) / 1e9,
+        "unique_kv_GBps": unique / (dec * 1e-3) / 1e9,
+        "frac_hbm_peak_unique": unique / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+    }
+    return out
+
+
+def calibrate_copy(torch):
+    """Plain device-to-device copies of 1 GiB: 1 GiB read and 1 GiB written per
+    copy kernel, the reference for scaling the HBM byte counters."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
 def main():
@@ -136,6 +224,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load_library()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     w = wl.llama_gqa_decode(pool_fill="zero", partition_size=args.partition_size,
                             fixed_context=args.fixed_context)
@@ -144,30 +235,16 @@ def main():
     kv_bytes = w.kv_bytes_read()
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        g.step()
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        g.slot_mapping()
-        g.write()
-        ev[i][0].record(stream)
-        g.attend()
-        ev[i][1].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    decode_ms = [a.elapsed_time(b) for a, b in ev]
-    step_ms = total_ms / K
+    step_ms, decode_ms = timed(torch, stream, K, args.warmup,
+                               lambda: (g.slot_mapping(), g.write()), g.attend)
     dec_avg_ms = float(np.mean(decode_ms))
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    sum_ctx = int(w.context_lens.astype(np.int64).sum())
+    del g
+    torch.cuda.empty_cache()
 
+    sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 3)
     cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
 
     traffic = measured_traffic(w.name, args.partition_size)
@@ -195,7 +272,7 @@ def main():
             "num_blocks": w.num_blocks,
             "context_lens": ("fixed %d" % args.fixed_context) if args.fixed_context
             else "uniform [1, 8192], seed 87003",
-            "sum_context_tokens": int(w.context_lens.astype(np.int64).sum()),
+            "sum_context_tokens": sum_ctx,
             "kv_bytes_per_step": kv_bytes,
             "partition_size": args.partition_size,
         },
@@ -203,7 +280,7 @@ def main():
                       "p50": float(np.percentile(decode_ms, 50)) * 1e3,
                       "p90": float(np.percentile(decode_ms, 90)) * 1e3},
         "roofline": {
-            "kernel": "pa_decode (partition kernel + log-sum-exp merge)",
+            "kernel": "pa_decode (persistent partition kernel + log-sum-exp merge)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -212,6 +289,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
+        "secondary": sec,
     }
     print(json.dumps(rec), flush=True)
 

@@ -1,0 +1,196 @@
+"""The C ABI without a GPU: libpa.so loads, exports every entry point that
+include/pa.h declares, and rejects bad arguments on the host (status codes,
+error text) before anything is enqueued.  Only argument checks that fail
+before the HIP runtime is touched are exercised here.  CPU only."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_87_amd import binding as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+FAKE = 0x10000          # a 16-byte-aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.skip("libpa.so not built")
+    return pa.load_library()
+
+
+def pool(**kw):
+    d = dict(k_cache=FAKE, v_cache=FAKE, num_blocks=64, block_size=16, num_kv_heads=2,
+             head_dim=128, dtype=pa.PA_BF16)
+    d.update(kw)
+    return pa.PaKVPool(**d)
+
+
+def seqs(**kw):
+    d = dict(block_tables=FAKE, context_lens=FAKE, num_seqs=4, max_blocks_per_seq=8,
+             max_context_len=128)
+    d.update(kw)
+    return pa.PaSeqDesc(**d)
+
+
+def test_header_declares_the_hot_path():
+    fns = header_functions()
+    for name in ("pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
+                 "pa_prefill", "pa_status_string", "pa_last_error", "pa_version"):
+        assert name in fns
+    assert set(fns) == set(pa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pa_status_string(pa.PA_OK) == b"PA_OK"
+    assert lib.pa_status_string(pa.PA_ERR_INVALID_ARG) == b"PA_ERR_INVALID_ARG"
+    assert lib.pa_status_string(pa.PA_ERR_UNSUPPORTED) == b"PA_ERR_UNSUPPORTED"
+    assert lib.pa_status_string(pa.PA_ERR_WORKSPACE) == b"PA_ERR_WORKSPACE"
+    assert lib.pa_status_string(pa.PA_ERR_HIP) == b"PA_ERR_HIP"
+    assert lib.pa_status_string(12345) == b"PA_ERR_UNKNOWN"
+    assert lib.pa_version() >> 16 == 1
+
+
+def decode(lib, p, s, q=FAKE, out=FAKE, hq=8, scale=0.1, part=0, ws=None, ws_bytes=0):
+    return lib.pa_decode(ctypes.byref(p), ctypes.byref(s), q, out, hq, scale, part, ws, ws_bytes,
+                         None)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(k_cache=0), pa.PA_ERR_INVALID_ARG),
+    (dict(v_cache=FAKE + 8), pa.PA_ERR_INVALID_ARG),        # misaligned
+    (dict(num_blocks=0), pa.PA_ERR_INVALID_ARG),
+    (dict(dtype=7), pa.PA_ERR_INVALID_ARG),
+    (dict(block_size=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_pools(lib, change, status):
+    assert decode(lib, pool(**change), seqs()) == status
+    assert lib.pa_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=5), pa.PA_ERR_INVALID_ARG),                   # not a multiple of num_kv_heads
+    (dict(hq=32), pa.PA_ERR_UNSUPPORTED),                  # n_rep 16
+    (dict(hq=0), pa.PA_ERR_INVALID_ARG),
+    (dict(part=24), pa.PA_ERR_INVALID_ARG),                # not a multiple of block_size
+    (dict(part=-16), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(q=0), pa.PA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), pa.PA_ERR_INVALID_ARG),
+    (dict(part=16), pa.PA_ERR_WORKSPACE),                  # 8 partitions need a workspace
+    (dict(part=16, ws=FAKE, ws_bytes=100), pa.PA_ERR_WORKSPACE),
+    (dict(part=16, ws=FAKE + 16, ws_bytes=1 << 30), pa.PA_ERR_WORKSPACE),   # not 256-aligned
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert decode(lib, pool(), seqs(), **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(block_tables=0), pa.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), pa.PA_ERR_INVALID_ARG),
+    (dict(max_context_len=-5), pa.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=5000), pa.PA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_sequences(lib, change, status):
+    assert decode(lib, pool(), seqs(**change)) == status
+
+
+def test_empty_batches_enqueue_nothing(lib):
+    assert decode(lib, pool(), seqs(num_seqs=0)) == pa.PA_OK
+    p, s = pool(), seqs()
+    assert lib.pa_write_kv(ctypes.byref(p), FAKE, FAKE, FAKE, 0, None) == pa.PA_OK
+    assert lib.pa_slot_mapping(ctypes.byref(p), ctypes.byref(s), None, 0, FAKE, None) == pa.PA_OK
+    assert lib.pa_prefill(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, 0, 0, 8, 0.1,
+                          None) == pa.PA_OK
+
+
+def test_write_and_slot_mapping_checks(lib):
+    p, s = pool(), seqs()
+    assert lib.pa_write_kv(ctypes.byref(p), FAKE, FAKE, FAKE, -1, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(ctypes.byref(p), 0, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(ctypes.byref(p), FAKE + 2, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_write_kv(None, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
+    # without q_start_loc there is exactly one token per sequence
+    assert lib.pa_slot_mapping(ctypes.byref(p), ctypes.byref(s), None, 3, FAKE,
+                               None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_slot_mapping(ctypes.byref(p), ctypes.byref(s), None, 4, 0,
+                               None) == pa.PA_ERR_INVALID_ARG
+    s0 = seqs(num_seqs=0)
+    assert lib.pa_slot_mapping(ctypes.byref(p), ctypes.byref(s0), FAKE, 4, FAKE,
+                               None) == pa.PA_ERR_INVALID_ARG
+
+
+def test_prefill_checks(lib):
+    s = seqs()
+    f32 = pool(dtype=pa.PA_F32)
+    assert lib.pa_prefill(ctypes.byref(f32), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
+                          None) == pa.PA_ERR_UNSUPPORTED
+    d64 = pool(head_dim=64)
+    assert lib.pa_prefill(ctypes.byref(d64), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
+                          None) == pa.PA_ERR_UNSUPPORTED
+    p = pool()
+    assert lib.pa_prefill(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, 0, 10, 10, 8, 0.1,
+                          None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_prefill(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, -1, 10, 8, 0.1,
+                          None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_prefill(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 6, 0.1,
+                          None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_workspace_plan(lib):
+    def ws(S, hq, d, maxctx, part, width=512):
+        s = seqs(num_seqs=S, max_context_len=maxctx, max_blocks_per_seq=width)
+        return lib.pa_decode_workspace_bytes(ctypes.byref(s), hq, d, 16, part)
+
+    # one partition covers everything: no workspace
+    assert ws(64, 32, 128, 8192, 0) == 0
+    assert ws(64, 32, 128, 8192, 8192) == 0
+    assert ws(4, 8, 64, 100, 112) == 0
+    # S * Hq * NP rows of D floats (256-byte aligned), then 2 floats per row
+    rows = 64 * 32 * 16
+    o = rows * 128 * 4
+    assert ws(64, 32, 128, 8192, 512) == (o + 255) // 256 * 256 + rows * 2 * 4
+    rows = 3 * 12 * 2            # ceil(2039 / 1024) partitions
+    o = rows * 64 * 4
+    assert ws(3, 12, 64, 2039, 1024) == (o + 255) // 256 * 256 + rows * 2 * 4
+    # the table width caps the context
+    assert ws(2, 8, 128, 100000, 512, width=64) == ws(2, 8, 128, 1024, 512, width=64)
+    # invalid input reports 0
+    assert ws(2, 8, 128, 1024, 24) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    t = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    p = pa.KVPool(t, t.clone())
+    with pytest.raises(ValueError):
+        p.c()
+    with pytest.raises(ValueError):
+        pa.KVPool(t, torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16))
