@@ -51,6 +51,7 @@ constexpr float kNegBig = -1.0e30f;  // "no score yet": finite, so m - m stays 0
 constexpr int kChunkBlocks = 64 * kWaves;  // blocks whose table entries one load brings in
 constexpr int kRing = 2;                    // blocks per wave in the load ring
 constexpr float kRescaleLog2 = 8.f;         // reference-max slack before a rescale
+constexpr int kKVPolicy = 2;                // K/V loads are non-temporal: each byte is read once
 
 // Head index, relative to the lane's own head, held at position idx of the
 // reduce-scatter input when the group has 2^R heads.  Level k of the scatter
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const Rsrc rk = make_rsrc(kpool + off, ok ? block_bytes : 0u);
     const Rsrc rv = make_rsrc(vpool + off, ok ? block_bytes : 0u);
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) kf[uu] = load_frag_buf<NW>(rk, lane_off + uu * 4 * row_bytes);
+    for (int uu = 0; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) vf[uu] = load_frag_buf<NW>(rv, lane_off + uu * 4 * row_bytes);
+    for (int uu = 0; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
     return nvalid;
   };
 

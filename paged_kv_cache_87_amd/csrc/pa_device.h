@@ -84,21 +84,22 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
                                            static_cast<int>(bytes), kRsrcWord3);
 }
 
-template <int NW>
+// AUX is the instruction's cache-policy field (2 = non-temporal on gfx950).
+template <int NW, int AUX = 0>
 __device__ __forceinline__ Frag<NW> load_frag_buf(Rsrc r, uint32_t voff) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   Frag<NW> f;
   if constexpr (NW == 2) {
-    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, AUX);
     f.w[0] = x[0]; f.w[1] = x[1];
   } else if constexpr (NW == 4) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX);
     f.w[0] = x[0]; f.w[1] = x[1]; f.w[2] = x[2]; f.w[3] = x[3];
   } else {
     static_assert(NW == 8, "fragment width");
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-    const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, AUX);
+    const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, AUX);
     f.w[0] = x[0]; f.w[1] = x[1]; f.w[2] = x[2]; f.w[3] = x[3];
     f.w[4] = y[0]; f.w[5] = y[1]; f.w[6] = y[2]; f.w[7] = y[3];
   }
