@@ -4,12 +4,12 @@ Headline workload: Llama-style GQA decode -- batch 64, 32 query / 8 KV heads,
 head_dim 128, bf16 K/V, block size 16, contexts uniform in [1, 8192]
 (seeded), random block tables over a 40000-block pool.  One step is the whole
 hot path for one new token per sequence: slot mapping, the K/V write of the
-new token, the partitioned decode kernel and the log-sum-exp merge, all
-through libpa.so on torch's current stream, with every input already
+new token, and the partitioned decode kernel (whose last partition of each
+sequence and KV head does the log-sum-exp merge), all through libpa.so on torch's current stream, with every input already
 resident in HBM.
 
 Printed: one JSON line with whole-step throughput (K/V bytes read per
-second), the decode call's roofline (K/V bytes / decode+merge time against
+second), the decode call's roofline (K/V bytes / decode kernel time against
 8 TB/s, timed with events over the timed region), the CPU oracle timed on a
 bounded sample of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16) and of the
@@ -280,7 +280,7 @@ def main():
                       "p50": float(np.percentile(decode_ms, 50)) * 1e3,
                       "p90": float(np.percentile(decode_ms, 90)) * 1e3},
         "roofline": {
-            "kernel": "pa_decode (persistent partition kernel + log-sum-exp merge)",
+            "kernel": "pa_decode (persistent partition kernel, log-sum-exp merge fused)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

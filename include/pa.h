@@ -140,15 +140,21 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
                       hipStream_t stream);
 
 /*
- * pa_decode_workspace_bytes -- device workspace pa_decode needs.
+ * pa_decode_workspace_bytes -- device workspace pa_decode needs for this
+ * pool, batch shape, num_q_heads and partition_size (only the pool's sizes
+ * are read, not its pointers).
  *
- * 0 when one partition covers max_context_len (partition_size 0 or >=
- * the longest context): the kernel then writes `out` directly.  Host only;
- * returns 0 for invalid arguments too (pa_decode then reports them).
+ * 0 when the context is not split (partition_size 0 or >= the longest
+ * context): the kernel then writes `out` directly.  Otherwise 256 KiB of
+ * arrival counters, then 2 * V * n_rep * head_dim floats of partial outputs
+ * (padded to 256 bytes), then 2 * V * n_rep * 2 floats of (max, sum), with
+ * V = min(2048, ceil(num_kv_heads * num_seqs * ceil(max_context_len / 16) /
+ * (partition_size / 16))) the most slices a call can use.  Host only, needs
+ * no device; returns 0 for invalid arguments too (pa_decode then reports
+ * them).
  */
-size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads,
-                                 int32_t head_dim, int32_t block_size,
-                                 int32_t partition_size);
+size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                                 int32_t num_q_heads, int32_t partition_size);
 
 /*
  * pa_decode -- attention of one new query row per (sequence, query head)
@@ -166,15 +172,27 @@ size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads,
  * are in the pool's dtype, 16-byte aligned; out is rounded to nearest even
  * for bf16.  Accumulation is fp32.
  *
- * partition_size: 0 = one pass per (sequence, KV head).  Otherwise a multiple
- * of block_size: each sequence's context is split into partitions of that
- * many tokens that are processed in parallel, each keeping its own maximum,
- * sum and normalised output, and a second kernel merges them by
- * log-sum-exp weighting.  The workspace (device, 256-byte aligned, at least
- * pa_decode_workspace_bytes(...)) holds the per-partition results; its
- * contents on entry do not matter.
+ * partition_size: 0 (or at least the longest context) = each (sequence, KV
+ * head) pair in one pass.  Otherwise a multiple of block_size that turns on
+ * the split-context decode: the blocks of all pairs, laid end to end, are cut
+ * into equal slices of at least partition_size tokens, one per workgroup that
+ * the GPU holds at once, so every workgroup reads the same number of bytes
+ * whatever the mix of context lengths.  A pair cut by slice boundaries is
+ * computed in pieces, each keeping its own maximum, sum and normalised
+ * output, and the workgroup that finishes its last piece merges them by
+ * log-sum-exp weighting, in the same kernel.
  *
- * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}; num_seqs <= 4096.
+ * workspace (device, 256-byte aligned, at least pa_decode_workspace_bytes(...)
+ * bytes; may be NULL when that is 0): its first 256 KiB hold one arrival
+ * counter per (sequence, KV head), the rest the pieces' results.  The
+ * counters must be zero before the first call that uses the workspace (zero
+ * the whole buffer once when allocating it); every call leaves them zero
+ * again, so one workspace serves any later batch shape.  The rest's contents
+ * on entry do not matter.  Calls that share a workspace must not overlap.
+ *
+ * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}; num_seqs <= 4096;
+ * num_kv_heads * num_seqs * ceil(max_context_len / 16) < 2^31; split,
+ * num_seqs * num_kv_heads <= 65536.
  */
 pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
                     void* out, int32_t num_q_heads, float scale, int32_t partition_size,

@@ -77,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "pa_slot_mapping": (i32, [pool_p, seq_p, vp, i32, vp, vp]),
         "pa_write_kv": (i32, [pool_p, vp, vp, vp, i32, vp]),
-        "pa_decode_workspace_bytes": (sz, [seq_p, i32, i32, i32, i32]),
+        "pa_decode_workspace_bytes": (sz, [pool_p, seq_p, i32, i32]),
         "pa_decode": (i32, [pool_p, seq_p, vp, vp, i32, f32, i32, vp, sz, vp]),
         "pa_prefill": (i32, [pool_p, seq_p, vp, vp, vp, i32, i32, i32, f32, vp]),
         "pa_status_string": (ctypes.c_char_p, [i32]),
@@ -198,11 +198,20 @@ def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
     _check("pa_write_kv", st)
 
 
-def pa_decode_workspace_bytes(seqs: SeqDesc, num_q_heads: int, head_dim: int, block_size: int,
+def pa_decode_workspace_bytes(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
                               partition_size: int) -> int:
-    cs = seqs.c()
-    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(cs), num_q_heads, head_dim,
-                                                        block_size, partition_size))
+    cp, cs = pool.c(), seqs.c()
+    return int(load_library().pa_decode_workspace_bytes(ctypes.byref(cp), ctypes.byref(cs),
+                                                        num_q_heads, partition_size))
+
+
+def decode_workspace(pool: KVPool, seqs: SeqDesc, num_q_heads: int, partition_size: int,
+                     device="cuda") -> Optional[torch.Tensor]:
+    """A zeroed workspace for pa_decode (None when none is needed).  Zeroing
+    once at allocation is what the library asks; every call leaves the
+    counter header zero again, so the tensor can be reused for any batch."""
+    need = pa_decode_workspace_bytes(pool, seqs, num_q_heads, partition_size)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
 
 
 def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, scale: float,
@@ -246,6 +255,6 @@ def pa_version() -> int:
 __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
-    "pa_decode", "pa_prefill", "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
+    "decode_workspace", "pa_decode", "pa_prefill", "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
     "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_F32", "PA_BF16",
 ]

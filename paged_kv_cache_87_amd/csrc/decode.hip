@@ -6,9 +6,10 @@
 // the whole history through the block table in place).
 //
 // Work decomposition
-//   grid (partition, kv_head, sequence), 256 threads = 4 waves.  A
-//   partition is `partition_size` consecutive tokens (whole blocks); the
-//   waves of a workgroup take the partition's blocks round-robin.
+//   A persistent grid of 256-thread workgroups (4 waves) walks segments of
+//   (sequence, KV head) pairs: whole pairs, or equal slices of the batch's
+//   blocks when the context is split (see the driver below); the waves of a
+//   workgroup take a segment's blocks round-robin.
 //   Inside a wave the 64 lanes form four 16-lane DPP rows.  Row r handles
 //   tokens r, r+4, r+8, r+12 of the wave's current 16-token block; lane i of
 //   the row owns elements [i*D/16, (i+1)*D/16) of the head dimension, so one
@@ -31,10 +32,11 @@
 // probabilities and the rescale factor of all heads are broadcast back
 // along the row with DPP rotations for the P.V accumulation, which is fp32.
 //
-// End of a workgroup: rows and then waves are merged with the same
-// max/sum rescaling; a sequence that fits in one partition is normalised and
-// written to `out`, otherwise the partition's (m, l, o/l) go to the
-// workspace and merge_kernel combines partitions by log-sum-exp weights.
+// End of a segment: rows and then waves are merged with the same max/sum
+// rescaling; a whole pair is normalised and written to `out`, a piece of a
+// pair writes its (o/l, m, l) to the workspace, and the workgroup that
+// counts the last piece of the pair combines them by log-sum-exp weights (an
+// arrival counter per pair, no second kernel).
 
 #include <float.h>
 
@@ -161,25 +163,114 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   else static_cast<float*>(out)[idx] = v;
 }
 
-// Persistent driver.  Each workgroup first builds, in LDS, the list of work
-// units of the whole batch: unit = (sequence, partition, KV head), full
-// partitions first and each sequence's partial last partition after them (so
-// the short units fill the tail), KV head fastest (the heads of one partition
-// read the same physical blocks at about the same time).  It then takes
-// units blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized to what
-// the GPU holds at once, so no workgroup is launched only to find no work.
+// Partition results travel between workgroups that may sit on different
+// dies: device-scope atomic stores and loads, which go past the dies'
+// private caches.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge of the pieces of one (sequence, KV head) pair, for the
+// N query heads of its group: out = sum_j w_j o_j / sum_j w_j with
+// w_j = l_j * 2^(m_j - max m), o_j a piece's normalised output (JuliaPagedAttn
+// "Online Softmax": the same max/sum rescaling that joins two blocks joins
+// two pieces), taken in token order with a running maximum.  The pair covers
+// flat blocks [A, E); its piece in slice i sits in partial slot 2i, or 2i + 1
+// for the first slice when the pair starts inside it.  Each thread owns E_
+// output elements; the loads of eight pieces are issued together, so a merge
+// of up to eight pieces costs one memory round trip.
+constexpr int kMergeBatch = 8;
+
+template <typename T, int D, int N>
+__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, int A, int E,
+                                           int Q, int tid) {
+  constexpr int kOut = N * D;
+  constexpr int E_ = (kOut + kThreads - 1) / kThreads;
+  const int ia = A / Q;
+  const int n = (E - 1) / Q - ia + 1;
+  const bool first_tail = A != ia * Q;
+  float M[E_], wsum[E_], osum[E_];
+  int hd[E_], dd[E_];
+#pragma unroll
+  for (int e = 0; e < E_; ++e) {
+    const int o = min(tid + e * kThreads, kOut - 1);
+    hd[e] = o / D;
+    dd[e] = o - hd[e] * D;
+    M[e] = kNegBig;
+    wsum[e] = 0.f;
+    osum[e] = 0.f;
+  }
+  for (int j0 = 0; j0 < n; j0 += kMergeBatch) {
+    float mj[E_][kMergeBatch], lj[E_][kMergeBatch], oj[E_][kMergeBatch];
+#pragma unroll
+    for (int jj = 0; jj < kMergeBatch; ++jj) {
+      const int i = ia + min(j0 + jj, n - 1);   // past the end: reload the last, weight 0
+      const int slot = (i == ia && first_tail) ? 2 * i + 1 : 2 * i;
+#pragma unroll
+      for (int e = 0; e < E_; ++e) {
+        const int64_t r = static_cast<int64_t>(slot) * N + hd[e];
+        mj[e][jj] = load_shared(a.part_ml + r * 2);
+        lj[e][jj] = load_shared(a.part_ml + r * 2 + 1);
+        oj[e][jj] = load_shared(a.part_o + r * D + dd[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E_; ++e)
+#pragma unroll
+      for (int jj = 0; jj < kMergeBatch; ++jj) {
+        if (j0 + jj >= n) break;
+        if (mj[e][jj] > M[e]) {
+          const float c = fast_exp2(M[e] - mj[e][jj]);
+          wsum[e] *= c;
+          osum[e] *= c;
+          M[e] = mj[e][jj];
+        }
+        const float w = lj[e][jj] * fast_exp2(mj[e][jj] - M[e]);
+        wsum[e] += w;
+        osum[e] = fmaf(w, oj[e][jj], osum[e]);
+      }
+  }
+  const int64_t row0 = static_cast<int64_t>(s) * a.num_q_heads + g * N;
+#pragma unroll
+  for (int e = 0; e < E_; ++e) {
+    const int o = tid + e * kThreads;
+    if (o < kOut)
+      store_out<T>(a.out, row0 * D + o, osum[e] * (wsum[e] > 0.f ? 1.f / wsum[e] : 0.f));
+  }
+}
+
+// Persistent driver.  Each workgroup first builds, in LDS, the plan of the
+// whole batch: clamped context lengths and the prefix sum of blocks per KV
+// head.  Pair p = s * Hkv + g (sequence s, KV head g) owns nb_s =
+// ceil(L_s / 16) blocks, laid end to end at flat offset
+// A_p = Hkv * pre_s + g * nb_s, B blocks in all.
 //
-// Inside a unit the four waves take the partition's blocks round-robin, each
-// through a ring of kRing register buffers (kRing-1 blocks in flight while
-// one is computed).  Between units nothing drains: while unit u computes, the
-// table entries of unit u+1 are already loaded, and the query rows and first
-// ring blocks of unit u+1 are issued right after unit u's output stores, so
-// the memory pipe stays busy across unit boundaries.  Every wait the
-// compiler places inside the ring is then exact, because whatever reaches
-// the ring's loop header has the two primed blocks as its youngest loads.
+// Split (min_slice_blocks > 0): the flat range is cut into slices of
+// Q = max(ceil(B / grid), min_slice_blocks) blocks and workgroup i takes
+// slice i, so every workgroup streams the same number of bytes whatever the
+// mix of context lengths.  The part of a pair inside a slice (a segment)
+// keeps its own online-softmax state.  Only the first and the last segment
+// of a slice can be pieces of a pair that goes on in another slice; they
+// write (o, m, l) to partial slots 2i and 2i + 1, the segments between them
+// are whole pairs and write `out`.  At the end of its slice a workgroup
+// counts its pieces at their pairs' arrival counters, and the last arrival
+// of a pair merges it.  Without a split, workgroup i takes pairs i,
+// i + grid, ... whole.
 //
-// Plan in dynamic LDS: ctx[S] clamped context lengths, pre_full[S+1] and
-// pre_part[S+1] exclusive prefix sums of the full / partial partition counts.
+// Inside a segment the four waves take its blocks round-robin, each through
+// a ring of kRing register buffers (kRing-1 blocks in flight while one is
+// computed).  Between segments nothing drains: while one computes, the table
+// entries of the next are already loaded, and the query rows and first ring
+// blocks of the next are issued right after the output stores, so the memory
+// pipe stays busy across boundaries.  Every wait the compiler places inside
+// the ring is then exact, because whatever reaches the ring's loop header has
+// the primed blocks as its youngest loads.
+//
+// Plan in dynamic LDS: ctx[S] clamped context lengths, pre[S+1] exclusive
+// prefix sum of blocks per KV head.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   using LT = Layout<T, D>;
@@ -190,16 +281,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   using F = Frag<NW>;
 
   extern __shared__ int32_t sm_plan[];
-  __shared__ int32_t sm_scan[2][kThreads];
+  __shared__ int32_t sm_scan[kThreads];
   __shared__ float sm_acc[kWaves][N][D];
   __shared__ float sm_m[kWaves][N];
   __shared__ float sm_l[kWaves][N];
+  __shared__ int sm_last[2];
 
   const int S = a.num_seqs;
-  const int P = a.partition_size;
+  const int Hkv = a.num_kv_heads;
   int32_t* const sm_ctx = sm_plan;
-  int32_t* const sm_pf = sm_plan + S;
-  int32_t* const sm_pp = sm_pf + S + 1;
+  int32_t* const sm_pre = sm_plan + S;
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
@@ -211,103 +302,117 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int per = (S + kThreads - 1) / kThreads;   // run of sequences per thread
     const int b0 = min(S, tid * per);
     const int b1 = min(S, b0 + per);
-    int cf = 0, cp = 0;
+    int cb = 0;
     for (int q = b0; q < b1; ++q) {
       int L = a.context_lens[q];
       L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
       sm_ctx[q] = L;
-      cf += L / P;
-      cp += (L % P != 0 || L == 0) ? 1 : 0;
+      cb += (L + kBlockSize - 1) / kBlockSize;
     }
-    sm_scan[0][tid] = cf;
-    sm_scan[1][tid] = cp;
+    sm_scan[tid] = cb;
     __syncthreads();
     if (tid < 64) {
       // exclusive scan of the 256 per-thread counts: 4 per lane, then the wave
-      int f[4], pp[4], tf = 0, tp = 0;
+      int c[4], t = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f[i] = sm_scan[0][4 * tid + i];
-        pp[i] = sm_scan[1][4 * tid + i];
-        tf += f[i];
-        tp += pp[i];
+        c[i] = sm_scan[4 * tid + i];
+        t += c[i];
       }
-      int xf = tf, xp = tp;
+      int x = t;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const int yf = __shfl_up(xf, off);
-        const int yp = __shfl_up(xp, off);
-        if (tid >= off) { xf += yf; xp += yp; }
+        const int y = __shfl_up(x, off);
+        if (tid >= off) x += y;
       }
-      int ef = xf - tf, ep = xp - tp;
+      int e = x - t;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sm_scan[0][4 * tid + i] = ef;
-        sm_scan[1][4 * tid + i] = ep;
-        ef += f[i];
-        ep += pp[i];
+        sm_scan[4 * tid + i] = e;
+        e += c[i];
       }
-      if (tid == 63) {
-        sm_pf[S] = xf;
-        sm_pp[S] = xp;
-      }
+      if (tid == 63) sm_pre[S] = x;
     }
     __syncthreads();
-    int ef = sm_scan[0][tid], ep = sm_scan[1][tid];
+    int e = sm_scan[tid];
     for (int q = b0; q < b1; ++q) {
-      const int L = sm_ctx[q];
-      sm_pf[q] = ef;
-      sm_pp[q] = ep;
-      ef += L / P;
-      ep += (L % P != 0 || L == 0) ? 1 : 0;
+      sm_pre[q] = e;
+      e += (sm_ctx[q] + kBlockSize - 1) / kBlockSize;
     }
     __syncthreads();
   }
-  const int n_full = sm_pf[S];
-  const int n_units = (n_full + sm_pp[S]) * a.num_kv_heads;
-
-  // ---- unit description --------------------------------------------------------
-  struct Unit {
-    int s, part, g, L, tok1, blk0, blk1, npart;
-  };
-  // last sequence q with pre[q] <= r (runs of equal prefixes end at the
-  // sequence that owns the unit)
-  auto owner = [&](const int32_t* pre, int r) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= r) lo = mid; else hi = mid - 1;
+  // an empty context gives zeros: its sequence's rows, spread over the grid
+  for (int q = blockIdx.x; q < S; q += gridDim.x) {
+    if (sm_ctx[q] == 0) {
+      for (int o = tid; o < a.num_q_heads * D; o += kThreads)
+        store_out<T>(a.out, static_cast<int64_t>(q) * a.num_q_heads * D + o, 0.f);
     }
-    return lo;
+  }
+
+  // ---- segments ---------------------------------------------------------------
+  const bool split = a.min_slice_blocks > 0;
+  const int n_pairs = S * Hkv;
+  const int B = Hkv * sm_pre[S];               // the host keeps this below 2^31
+  int Q = 1, F0 = 0, F1 = 0;                   // this workgroup's slice [F0, F1)
+  if (split) {
+    Q = max((B + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x),
+            a.min_slice_blocks);
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * Q;
+    F0 = static_cast<int>(f0 < B ? f0 : B);
+    F1 = static_cast<int>(f0 + Q < B ? f0 + Q : B);
+  }
+  auto nb_of = [&](int q) { return sm_pre[q + 1] - sm_pre[q]; };
+  struct Seg {
+    int s, g, L, tok1, blk0, blk1;
+    int slot;                        // partial slot, or -1: a whole pair, written to out
   };
-  auto unit_at = [&](int u) {
-    Unit x;
-    x.g = u % a.num_kv_heads;
-    const int r = u / a.num_kv_heads;
-    if (r < n_full) {
-      x.s = owner(sm_pf, r);
-      x.part = r - sm_pf[x.s];
+  // segment starting at `pos`: a flat block (split) or a pair index
+  auto seg_at = [&](int pos) {
+    Seg x;
+    if (split) {
+      // last sequence whose blocks start at or before pos (a run of empty
+      // sequences ends at the one that owns the block)
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (Hkv * sm_pre[mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      x.s = lo;
+      const int nb = nb_of(lo);
+      const int off = pos - Hkv * sm_pre[lo];
+      x.g = off / nb;
+      x.blk0 = off - x.g * nb;
+      x.blk1 = min(nb, x.blk0 + (F1 - pos));
+      x.slot = (x.blk0 == 0 && x.blk1 == nb) ? -1
+             : 2 * static_cast<int>(blockIdx.x) + (pos == F0 ? 0 : 1);
     } else {
-      x.s = owner(sm_pp, r - n_full);
-      x.part = sm_ctx[x.s] / P;
+      x.s = pos / Hkv;
+      x.g = pos - x.s * Hkv;
+      x.blk0 = 0;
+      x.blk1 = nb_of(x.s);
+      x.slot = -1;
     }
     x.L = sm_ctx[x.s];
-    x.npart = x.L > 0 ? (x.L + P - 1) / P : 1;
-    const int tok0 = x.part * P;
-    x.tok1 = (tok0 + P < x.L) ? tok0 + P : x.L;
-    x.blk0 = tok0 / kBlockSize;
-    x.blk1 = (x.tok1 + kBlockSize - 1) / kBlockSize;
+    x.tok1 = min(x.blk1 * kBlockSize, x.L);
     return x;
   };
+  auto skip_empty = [&](int p) {
+    while (p < n_pairs && nb_of(p / Hkv) == 0) p += gridDim.x;
+    return p;
+  };
+  auto next_pos = [&](const Seg& x, int pos) {
+    return split ? pos + (x.blk1 - x.blk0) : skip_empty(pos + gridDim.x);
+  };
+  const int pos_end = split ? F1 : n_pairs;
   // lane t: table entry of this wave's t-th block of the chunk at c0
-  auto load_tbl = [&](const Unit& x, int c0) {
+  auto load_tbl = [&](const Seg& x, int c0) {
     const int j = c0 + wave + kWaves * lane;
-    const int lim = min(x.blk0 + P / kBlockSize, a.max_blocks_per_seq);
+    const int lim = min(x.blk1, a.max_blocks_per_seq);
     return j < lim ? a.block_tables[static_cast<int64_t>(x.s) * a.max_blocks_per_seq + j] : -1;
   };
   const int own = li >> (4 - R);     // head whose full score this lane ends with
-  // query rows of the unit's heads, in this lane's scatter order
-  auto load_q = [&](const Unit& x, uint32_t (&qd)[N][NW]) {
+  // query rows of the segment's heads, in this lane's scatter order
+  auto load_q = [&](const Seg& x, uint32_t (&qd)[N][NW]) {
     const char* qb = static_cast<const char*>(a.q) +
                      ((static_cast<int64_t>(x.s) * a.num_q_heads + x.g * N) * D + li * EPL) * LT::kElt;
 #pragma unroll
@@ -328,20 +433,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const char* vpool = static_cast<const char*>(a.v_cache);
   const float sl2 = a.scale_log2;
 
-  // ---- current unit state -------------------------------------------------------
-  int u = blockIdx.x;
-  if (u >= n_units) return;
-  Unit cur = unit_at(u);
+  // ---- current segment state ----------------------------------------------------
+  int pos = split ? F0 : skip_empty(blockIdx.x);
+  if (pos >= pos_end) return;
+  Seg cur = seg_at(pos);
   int c0 = cur.blk0;                 // first block of the current chunk
   int nk = 0;                        // this wave's blocks in the current chunk
   int tbl = load_tbl(cur, c0);
   uint32_t qv[N][NW];
   load_q(cur, qv);
   uint32_t lane_off = (cur.g * D + li * EPL) * LT::kElt + row * row_bytes;
-  auto chunk_blocks = [&](const Unit& x, int cs) {
+  auto chunk_blocks = [&](const Seg& x, int cs) {
     const int ce = min(x.blk1, cs + kChunkBlocks);
     return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
   };
+
+  // pieces of pairs stored by this slice: its first segment (slot 2i) and its
+  // last (slot 2i + 1), counted at the end
+  int pa_s = -1, pa_g = 0, pb_s = -1, pb_g = 0;
 
   float m = kNegBig, l = 0.f;
   float acc[N][EPL];
@@ -470,12 +579,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- prologue: the first unit's table and query rows, then the next unit's
-  // (left in flight), then the first unit's primed ring blocks -----------------
+  // ---- prologue: the first segment's table and query rows, then the next one's
+  // (left in flight), then the first segment's primed ring blocks --------------
   __builtin_amdgcn_s_waitcnt(0);
-  int un = u + gridDim.x;
-  bool has_next = un < n_units;
-  Unit nxt = has_next ? unit_at(un) : cur;
+  int pos_n = next_pos(cur, pos);
+  bool has_next = pos_n < pos_end;
+  Seg nxt = has_next ? seg_at(pos_n) : cur;
   int tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
   nk = chunk_blocks(cur, c0);
 
@@ -488,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int n2 = 0;
 
   for (;;) {
-    // ---- the ring over this chunk of the current unit (one exit, at the
+    // ---- the ring over this chunk of the current segment (one exit, at the
     // bottom: a trip always runs every stage; stages past the wave's last
     // block see size-0 descriptors and zero valid tokens and change nothing)
     if constexpr (kRing == 2) {
@@ -514,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- a partition longer than one chunk: next chunk of the same unit ------
+    // ---- a segment longer than one chunk: next chunk of the same segment -----
     if (c0 + kChunkBlocks < cur.blk1) {
       c0 += kChunkBlocks;
       tbl = load_tbl(cur, c0);
@@ -562,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
     {
-      const bool direct = cur.npart == 1;
+      const bool direct = cur.slot < 0;
       for (int o = tid; o < N * D; o += kThreads) {
         const int h = o / D;
         const int d = o - h * D;
@@ -581,26 +690,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         if (direct) {
           store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
         } else {
-          const int64_t pi =
-              (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * a.num_partitions + cur.part;
-          a.part_o[pi * D + d] = val;
+          const int64_t pi = static_cast<int64_t>(cur.slot) * N + h;
+          store_shared(a.part_o + pi * D + d, val);
           if (d == 0) {
-            a.part_ml[pi * 2 + 0] = M;
-            a.part_ml[pi * 2 + 1] = lsum;
+            store_shared(a.part_ml + pi * 2 + 0, M);
+            store_shared(a.part_ml + pi * 2 + 1, lsum);
           }
         }
       }
     }
-    __syncthreads();   // LDS merge buffers are reused by the next unit
+    __syncthreads();   // LDS merge buffers are reused by the next segment
+    if (cur.slot >= 0) {
+      if (cur.slot & 1) { pb_s = cur.s; pb_g = cur.g; }
+      else { pa_s = cur.s; pa_g = cur.g; }
+    }
     if (!has_next) break;
 
-    // ---- move on: loads of the unit after next, then the next unit's primed
-    // ring blocks (in that order, so the primed blocks are the youngest loads)
+    // ---- move on: loads of the segment after next, then the next segment's
+    // primed ring blocks (in that order, so the primed blocks are the
+    // youngest loads)
     cur = nxt;
-    u = un;
-    un = u + gridDim.x;
-    has_next = un < n_units;
-    if (has_next) nxt = unit_at(un);
+    pos = pos_n;
+    pos_n = next_pos(cur, pos);
+    has_next = pos_n < pos_end;
+    if (has_next) nxt = seg_at(pos_n);
     tbl = tbl_nxt;
     load_q(cur, qv);
     tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
@@ -618,88 +731,90 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if constexpr (kRing == 3) n1 = issue(1, k1, v1);
     __builtin_amdgcn_sched_barrier(0);
   }
-}
 
-// Log-sum-exp merge of the partitions of one (sequence, query head):
-// out = sum_j w_j o_j / sum_j w_j with w_j = l_j * 2^(m_j - max m).
-// One wave per row; the partition maxima are read lane-parallel, then every
-// lane accumulates D/64 output elements over the partitions.
-constexpr int kMergeThreads = 64;
-
-template <typename T, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  constexpr int E = D / kMergeThreads;
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int lane = threadIdx.x;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
-  const int npart = L > 0 ? (L + a.partition_size - 1) / a.partition_size : 1;
-  if (npart <= 1) return;  // the decode kernel wrote this row itself
-  const int64_t base = (static_cast<int64_t>(s) * a.num_q_heads + h) * a.num_partitions;
-  const float* ml = a.part_ml + base * 2;
-  const float* po = a.part_o + base * D;
-  float M = kNegBig;
-  for (int j = lane; j < npart; j += kMergeThreads) M = fmaxf(M, ml[2 * j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float wsum = 0.f;
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < npart; ++j) {
-    const float w = ml[2 * j + 1] * fast_exp2(ml[2 * j] - M);
-    wsum += w;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[static_cast<int64_t>(j) * D + lane + e * kMergeThreads], o[e]);
+  // ---- arrivals of this slice's pieces ------------------------------------------
+  // The pieces' stores bypass the dies' private caches; once every wave has
+  // waited for its stores they are visible device-wide, before the count
+  // moves.  The last arrival of a pair merges its pieces and leaves the
+  // counter at zero for the next call.
+  if (pa_s >= 0 || pb_s >= 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto pair_start = [&](int q, int g) { return Hkv * sm_pre[q] + g * nb_of(q); };
+    auto pieces = [&](int q, int g) {
+      const int A = pair_start(q, g);
+      return (A + nb_of(q) - 1) / Q - A / Q + 1;
+    };
+    if (tid == 0) {
+      int last_a = 0, last_b = 0;
+      if (pa_s >= 0)
+        last_a = __hip_atomic_fetch_add(a.counters + pa_s * Hkv + pa_g, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == pieces(pa_s, pa_g) - 1;
+      if (pb_s >= 0)
+        last_b = __hip_atomic_fetch_add(a.counters + pb_s * Hkv + pb_g, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == pieces(pb_s, pb_g) - 1;
+      sm_last[0] = last_a;
+      sm_last[1] = last_b;
+    }
+    __syncthreads();
+    if (sm_last[0]) {
+      const int A = pair_start(pa_s, pa_g);
+      merge_pair<T, D, N>(a, pa_s, pa_g, A, A + nb_of(pa_s), Q, tid);
+      if (tid == 0)
+        __hip_atomic_store(a.counters + pa_s * Hkv + pa_g, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (sm_last[1]) {
+      const int A = pair_start(pb_s, pb_g);
+      merge_pair<T, D, N>(a, pb_s, pb_g, A, A + nb_of(pb_s), Q, tid);
+      if (tid == 0)
+        __hip_atomic_store(a.counters + pb_s * Hkv + pb_g, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const int64_t out_base = (static_cast<int64_t>(s) * a.num_q_heads + h) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) store_out<T>(a.out, out_base + lane + e * kMergeThreads, o[e] * inv);
 }
 
+// The persistent grid: what the device holds at once, but no more
+// workgroups than there are slices (split) or pairs (whole pairs).
 template <typename T, int D, int R>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+hipError_t run_typed(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = plan_lds_bytes(a.num_seqs);
   const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R>);
   int resident = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &resident);
   if (e != hipSuccess) return e;
-  const int64_t max_units =
-      static_cast<int64_t>(a.num_partitions) * a.num_kv_heads * a.num_seqs;
-  const int grid = static_cast<int>(resident < max_units ? resident : max_units);
+  const int64_t work = a.min_slice_blocks > 0
+                           ? static_cast<int64_t>(a.max_slices)
+                           : static_cast<int64_t>(a.num_kv_heads) * a.num_seqs;
+  const int grid = static_cast<int>(resident < work ? resident : (work > 0 ? work : 1));
   hipLaunchKernelGGL((decode_kernel<T, D, R>), dim3(grid), dim3(kThreads), lds, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.num_partitions == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
-                     stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_heads(const DecodeArgs& a, hipStream_t stream) {
+hipError_t run_heads(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_typed<T, D, 0>(a, stream);
-    case 2: return launch_typed<T, D, 1>(a, stream);
-    case 4: return launch_typed<T, D, 2>(a, stream);
-    case 8: return launch_typed<T, D, 3>(a, stream);
+    case 1: return run_typed<T, D, 0>(a, stream);
+    case 2: return run_typed<T, D, 1>(a, stream);
+    case 4: return run_typed<T, D, 2>(a, stream);
+    case 8: return run_typed<T, D, 3>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t run(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype == 1) {
-    if (a.head_dim == 128) return launch_heads<uint16_t, 128>(a, stream);
-    if (a.head_dim == 64) return launch_heads<uint16_t, 64>(a, stream);
+    if (a.head_dim == 128) return run_heads<uint16_t, 128>(a, stream);
+    if (a.head_dim == 64) return run_heads<uint16_t, 64>(a, stream);
   } else {
-    if (a.head_dim == 128) return launch_heads<float, 128>(a, stream);
-    if (a.head_dim == 64) return launch_heads<float, 64>(a, stream);
+    if (a.head_dim == 128) return run_heads<float, 128>(a, stream);
+    if (a.head_dim == 64) return run_heads<float, 64>(a, stream);
   }
   return hipErrorInvalidValue;
 }
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) { return run(a, stream); }
 
 }  // namespace pa

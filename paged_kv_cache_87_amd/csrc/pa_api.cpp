@@ -1,5 +1,5 @@
 // C-ABI entry points of libpa.so: host-side argument checks, the decode
-// partition plan and the mapping of HIP errors to status codes.  Every
+// split plan and the mapping of HIP errors to status codes.  Every
 // check runs before anything is enqueued; no entry point allocates.
 
 #include <hip/hip_runtime.h>
@@ -124,25 +124,23 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
 }
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                       int32_t num_q_heads, int32_t head_dim, int32_t partition_size) {
+                       int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                       int32_t partition_size) {
   DecodePlan p{};
   const int64_t by_table = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
   p.context_cap = static_cast<int32_t>(max_context_len < by_table ? max_context_len : by_table);
-  const int32_t cover = ((p.context_cap > 0 ? p.context_cap : 1) + kBlockSize - 1) /
-                        kBlockSize * kBlockSize;
-  if (partition_size <= 0 || partition_size >= cover) {
-    p.partition_size = cover;
-    p.num_partitions = 1;
-  } else {
-    p.partition_size = partition_size;
-    p.num_partitions = (p.context_cap + partition_size - 1) / partition_size;
-  }
-  if (p.num_partitions > 1) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.num_partitions;
-    const size_t o_bytes = rows * head_dim * sizeof(float);
-    p.part_ml_offset = (o_bytes + 255) / 256 * 256;
-    p.workspace_bytes = p.part_ml_offset + rows * 2 * sizeof(float);
-  }
+  const int64_t cap_blocks = (static_cast<int64_t>(p.context_cap) + kBlockSize - 1) / kBlockSize;
+  p.max_blocks = static_cast<int64_t>(num_kv_heads) * num_seqs * cap_blocks;
+  const int64_t cover = (cap_blocks > 0 ? cap_blocks : 1) * kBlockSize;
+  if (partition_size <= 0 || partition_size >= cover) return p;   // no split
+  p.min_slice_blocks = partition_size / kBlockSize;
+  const int64_t slices = (p.max_blocks + p.min_slice_blocks - 1) / p.min_slice_blocks;
+  p.max_slices = static_cast<int32_t>(slices < kMaxSlices ? (slices > 0 ? slices : 1)
+                                                          : kMaxSlices);
+  const size_t rows = static_cast<size_t>(2) * p.max_slices * (num_q_heads / num_kv_heads);
+  p.part_o_offset = kCounterHeaderBytes;
+  p.part_ml_offset = p.part_o_offset + (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  p.workspace_bytes = p.part_ml_offset + rows * 2 * sizeof(float);
   return p;
 }
 
@@ -201,14 +199,16 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
   return hip_status(pa::launch_write_kv(a, stream), "write_kv launch");
 }
 
-size_t pa_decode_workspace_bytes(const pa_seq_desc* seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t partition_size) {
-  if (seqs == nullptr || seqs->num_seqs < 0 || seqs->max_blocks_per_seq <= 0 ||
-      seqs->max_context_len < 0 || num_q_heads <= 0 || head_dim <= 0 ||
-      block_size != pa::kBlockSize || partition_size < 0 || partition_size % block_size != 0)
+size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                                 int32_t num_q_heads, int32_t partition_size) {
+  if (pool == nullptr || seqs == nullptr || seqs->num_seqs < 0 ||
+      seqs->max_blocks_per_seq <= 0 || seqs->max_context_len < 0 || pool->num_kv_heads <= 0 ||
+      pool->head_dim <= 0 || pool->block_size != pa::kBlockSize || num_q_heads <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0 || partition_size < 0 ||
+      partition_size % pool->block_size != 0)
     return 0;
   return pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, seqs->max_context_len,
-                         num_q_heads, head_dim, partition_size)
+                         pool->num_kv_heads, num_q_heads, pool->head_dim, partition_size)
       .workspace_bytes;
 }
 
@@ -229,22 +229,29 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   if (!aligned16(q) || !aligned16(out))
     return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   const pa::DecodePlan plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq,
-                                              seqs->max_context_len, num_q_heads,
-                                              pool->head_dim, partition_size);
-  if (plan.num_partitions > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "%d partitions (at most 65535)", plan.num_partitions);
+                                              seqs->max_context_len, pool->num_kv_heads,
+                                              num_q_heads, pool->head_dim, partition_size);
+  if (plan.max_blocks >= (int64_t(1) << 31))
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * num_seqs * context blocks = %lld (below 2^31)",
+                static_cast<long long>(plan.max_blocks));
   if (seqs->num_seqs > pa::kMaxDecodeSeqs)
     return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most %d)", seqs->num_seqs,
                 pa::kMaxDecodeSeqs);
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int32_t* counters = nullptr;
   if (plan.workspace_bytes > 0) {
+    if (static_cast<int64_t>(seqs->num_seqs) * pool->num_kv_heads > pa::kCounterSlots)
+      return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads = %lld (at most %d when split)",
+                  static_cast<long long>(seqs->num_seqs) * pool->num_kv_heads,
+                  pa::kCounterSlots);
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
                   plan.workspace_bytes, workspace == nullptr ? size_t(0) : workspace_bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    part_o = static_cast<float*>(workspace);
+    counters = static_cast<int32_t*>(workspace);
+    part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_offset);
     part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
   }
   pa::DecodeArgs a{};
@@ -256,6 +263,7 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   a.context_lens = seqs->context_lens;
   a.part_o = part_o;
   a.part_ml = part_ml;
+  a.counters = counters;
   a.num_seqs = seqs->num_seqs;
   a.num_blocks = pool->num_blocks;
   a.num_kv_heads = pool->num_kv_heads;
@@ -264,8 +272,8 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   a.dtype = pool->dtype;
   a.max_blocks_per_seq = seqs->max_blocks_per_seq;
   a.context_cap = plan.context_cap;
-  a.partition_size = plan.partition_size;
-  a.num_partitions = plan.num_partitions;
+  a.min_slice_blocks = plan.min_slice_blocks;
+  a.max_slices = plan.max_slices;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(pa::launch_decode(a, stream), "decode launch");
 }

@@ -41,8 +41,9 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_o;           // [num_seqs, num_q_heads, num_partitions, head_dim]
-  float* part_ml;          // [num_seqs, num_q_heads, num_partitions, 2]
+  float* part_o;           // [2 * max_slices, n_rep, head_dim] partial outputs
+  float* part_ml;          // [2 * max_slices, n_rep, 2] their (max, sum)
+  int32_t* counters;       // [num_seqs * num_kv_heads] arrivals, zero between calls
   int32_t num_seqs;
   int32_t num_blocks;
   int32_t num_kv_heads;
@@ -51,8 +52,8 @@ struct DecodeArgs {
   int32_t dtype;           // 0 = f32, 1 = bf16
   int32_t max_blocks_per_seq;
   int32_t context_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
-  int32_t partition_size;  // tokens per partition, multiple of the block size
-  int32_t num_partitions;  // ceil(context_cap / partition_size), >= 1
+  int32_t min_slice_blocks;  // 0: every (sequence, KV head) in one pass; else split
+  int32_t max_slices;      // split: upper bound of the grid (partial slots = 2x)
   float scale_log2;        // softmax scale * log2(e)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
@@ -79,10 +80,10 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Decode work plan kept in LDS by every workgroup: clamped context lengths and
-// two prefix-sum arrays over the batch.
+// the prefix sum of blocks per KV head over the batch.
 constexpr int kMaxDecodeSeqs = 4096;
 inline size_t plan_lds_bytes(int num_seqs) {
-  return (3 * static_cast<size_t>(num_seqs) + 2) * sizeof(int32_t);
+  return (2 * static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t);
 }
 
 // Workgroups of kernel `fn` (block size `threads`, `lds` bytes of dynamic
@@ -90,15 +91,26 @@ inline size_t plan_lds_bytes(int num_seqs) {
 // LDS size).
 hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out);
 
-// Partition plan shared by the workspace query and pa_decode.
+// Split decodes keep one arrival counter per (sequence, KV head) at the
+// start of the workspace, in a header of fixed size so that it stays in place
+// whatever the batch shape of the next call.
+constexpr int kCounterSlots = 65536;
+constexpr size_t kCounterHeaderBytes = kCounterSlots * sizeof(int32_t);
+// At most this many slices (workgroups) share a split decode.
+constexpr int kMaxSlices = 2048;
+
+// Split plan shared by the workspace query and pa_decode.
 struct DecodePlan {
   int32_t context_cap;
-  int32_t partition_size;
-  int32_t num_partitions;
+  int32_t min_slice_blocks;  // 0: no split
+  int32_t max_slices;
   size_t workspace_bytes;
-  size_t part_ml_offset;   // byte offset of part_ml inside the workspace
+  size_t part_o_offset;      // byte offsets inside the workspace
+  size_t part_ml_offset;
+  int64_t max_blocks;        // num_kv_heads * num_seqs * ceil(context_cap / block size)
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                       int32_t num_q_heads, int32_t head_dim, int32_t partition_size);
+                       int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                       int32_t partition_size);
 
 }  // namespace pa

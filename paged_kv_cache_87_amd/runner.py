@@ -68,9 +68,9 @@ class GpuStep:
         self.max_q_len = 0
         if w.q_start_loc is not None:
             self.max_q_len = int(np.diff(w.q_start_loc).max()) if w.num_seqs else 0
-        ws = pa.pa_decode_workspace_bytes(self.seqs, w.num_q_heads, w.head_dim, w.block_size,
-                                          self.partition_size) if w.kind == "decode" else 0
-        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
+        self.workspace = pa.decode_workspace(self.pool, self.seqs, w.num_q_heads,
+                                             self.partition_size,
+                                             device) if w.kind == "decode" else None
 
     # -- setup: history written before the step ------------------------------
     def write_history(self):
@@ -107,9 +107,7 @@ class GpuStep:
             ps = self.partition_size if partition_size is None else partition_size
             ws = self.workspace
             if partition_size is not None and partition_size != self.partition_size:
-                need = pa.pa_decode_workspace_bytes(self.seqs, w.num_q_heads, w.head_dim,
-                                                    w.block_size, ps)
-                ws = torch.empty(need, dtype=torch.uint8, device=self.device) if need else None
+                ws = pa.decode_workspace(self.pool, self.seqs, w.num_q_heads, ps, self.device)
             return pa.pa_decode(self.pool, self.seqs, self.q, self.out, w.scale, ps, ws)
         return pa.pa_prefill(self.pool, self.seqs, self.q, self.out, self.q_start_loc,
                              self.max_q_len, w.scale)

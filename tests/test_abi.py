@@ -121,6 +121,16 @@ def test_decode_rejects_bad_sequences(lib, change, status):
     assert decode(lib, pool(), seqs(**change)) == status
 
 
+def test_split_decode_counter_capacity(lib):
+    # 4096 sequences x 32 KV heads need more arrival counters than the header holds
+    p = pool(num_kv_heads=32)
+    s = seqs(num_seqs=4096, max_context_len=4096, max_blocks_per_seq=256)
+    assert decode(lib, p, s, hq=32, part=512, ws=FAKE, ws_bytes=1 << 40) == pa.PA_ERR_UNSUPPORTED
+    assert b"num_kv_heads" in lib.pa_last_error()
+    # unsplit, the same batch needs no counters
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(s), 32, 0) == 0
+
+
 def test_empty_batches_enqueue_nothing(lib):
     assert decode(lib, pool(), seqs(num_seqs=0)) == pa.PA_OK
     p, s = pool(), seqs()
@@ -164,25 +174,40 @@ def test_prefill_checks(lib):
 
 
 def test_workspace_plan(lib):
-    def ws(S, hq, d, maxctx, part, width=512):
+    def ws(S, hq, d, maxctx, part, width=512, hkv=2):
         s = seqs(num_seqs=S, max_context_len=maxctx, max_blocks_per_seq=width)
-        return lib.pa_decode_workspace_bytes(ctypes.byref(s), hq, d, 16, part)
+        p = pool(head_dim=d, num_kv_heads=hkv)
+        return lib.pa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(s), hq, part)
 
-    # one partition covers everything: no workspace
-    assert ws(64, 32, 128, 8192, 0) == 0
-    assert ws(64, 32, 128, 8192, 8192) == 0
+    # not split: no workspace
+    assert ws(64, 32, 128, 8192, 0, hkv=8) == 0
+    assert ws(64, 32, 128, 8192, 8192, hkv=8) == 0
     assert ws(4, 8, 64, 100, 112) == 0
-    # S * Hq * NP rows of D floats (256-byte aligned), then 2 floats per row
-    rows = 64 * 32 * 16
-    o = rows * 128 * 4
-    assert ws(64, 32, 128, 8192, 512) == (o + 255) // 256 * 256 + rows * 2 * 4
-    rows = 3 * 12 * 2            # ceil(2039 / 1024) partitions
-    o = rows * 64 * 4
-    assert ws(3, 12, 64, 2039, 1024) == (o + 255) // 256 * 256 + rows * 2 * 4
+    # a 256 KiB counter header, 2 V n_rep rows of D floats (256-byte aligned),
+    # then 2 floats per row; V = min(2048, ceil(Hkv S ceil(L/16) / (P/16)))
+    hdr = 256 * 1024
+
+    def expect(v, n_rep, d):
+        rows = 2 * v * n_rep
+        return hdr + (rows * d * 4 + 255) // 256 * 256 + rows * 2 * 4
+
+    # 8 * 64 * 512 blocks in slices of >= 32 blocks: capped at 2048 slices
+    assert ws(64, 32, 128, 8192, 512, hkv=8) == expect(2048, 4, 128)
+    # 2 * 3 * ceil(2039 / 16) = 768 blocks in slices of >= 64 blocks: 12
+    assert ws(3, 8, 64, 2039, 1024) == expect(12, 4, 64)
     # the table width caps the context
     assert ws(2, 8, 128, 100000, 512, width=64) == ws(2, 8, 128, 1024, 512, width=64)
     # invalid input reports 0
     assert ws(2, 8, 128, 1024, 24) == 0
+    assert ws(2, 7, 128, 1024, 512) == 0      # num_q_heads not a multiple of num_kv_heads
+    assert lib.pa_decode_workspace_bytes(None, None, 8, 512) == 0
+
+
+def test_decode_rejects_oversized_flat_range(lib):
+    # 64 KV heads x 4096 sequences x 16384 blocks do not fit the 31-bit flat block index
+    p = pool(num_kv_heads=64)
+    s = seqs(num_seqs=4096, max_context_len=16384 * 16, max_blocks_per_seq=16384)
+    assert decode(lib, p, s, hq=64) == pa.PA_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():
