@@ -15,7 +15,7 @@ bounded sample of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16) and of the
 long-context shared-prefix decode.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 
@@ -40,8 +40,8 @@ METRIC = "paged-attn decode μs/step + KV-read HBM GB/s (% of peak), batch 64 ct
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--partition-size", type=int, default=1024)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="wall-time budget of the CPU oracle sample")
