@@ -27,6 +27,10 @@ COMMON = [
 ]
 # Device code: no packed-fp32 instructions (v_pk_{add,mul,fma}_f32).
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags.  The prefill's matrix-core accumulators stay in
+# ordinary VGPRs: left to its default, the allocator parks them in AGPRs and
+# copies them back and forth around the softmax rescale every key tile.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -39,7 +43,8 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *COMMON, *DEVICE, *lang, "-c", src, "-o", obj]
+    extra = EXTRA.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON, *DEVICE, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msg = "\n".join(x for x in (r.stdout + r.stderr).splitlines() if noise not in x)

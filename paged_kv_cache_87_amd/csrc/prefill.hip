@@ -11,8 +11,9 @@
 //   K/V tile brought into LDS serves every head of the group.  Wave w owns
 //   columns 32w .. 32w+31.
 //   The keys are walked in tiles of 64 (four 16-token blocks, each found
-//   through the block table) up to the tile's last position; K is staged in
-//   LDS as [key][d], V transposed as [d][key], double-buffered.
+//   through the block table) up to the tile's last position; K and V are
+//   staged in LDS as [key][d] rows, double-buffered, with the block ids of
+//   the tile after next loaded while the next tile's K/V are in flight.
 //
 // Arithmetic (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
 //   S^T = K . Q^T   : keys on the M axis, the wave's 32 columns on N; the
@@ -22,10 +23,16 @@
 //   O^T += V^T . P^T: the accumulator layout of S^T, rounded to bf16, is
 //                     directly the B operand of the P.V product when the
 //                     contraction index k of lane half h is mapped to key
-//                     16c + 4h + (k mod 4) + 8 (k div 4) for 16-key step c;
-//                     the V^T fragments are read from LDS with the same map.
-//   Online softmax per column (running max / running sum); the reference max
-//   only moves when a score passes it by more than 2^8 (then O is rescaled).
+//                     16c + 4h + (k mod 4) + 8 (k div 4) for 16-key step c.
+//                     The V^T fragments (four consecutive keys of one d per
+//                     read) come from the [key][d] rows through gfx950's
+//                     transposing LDS read: in each 16-lane group, source
+//                     lane s addresses key row s/4 and d columns 4 (s mod 4)
+//                     .. +3, and lane i receives d column i of the four rows.
+//   Online softmax per column (running max / running sum) on the raw scores,
+//   scaled inside the exponent; the causal mask is applied only on the key
+//   tiles that reach past a column's position.  The reference max only moves
+//   when a score passes it by more than 2^8 (then O is rescaled).
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -39,19 +46,21 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kD = 128;               // head_dim handled here
 constexpr int kCols = 128;            // (head, token) columns per workgroup
 constexpr int kKeys = 64;             // keys per K/V tile (4 blocks)
-constexpr int kKStride = kD + 8;      // LDS row stride of K (bf16 elements)
-constexpr int kVStride = kKeys + 8;   // LDS row stride of V^T (bf16 elements)
+constexpr int kKStride = kD + 8;      // LDS row stride of K (bf16 elements): 68 dwords
+constexpr int kVStride = kD + 16;     // ... of V: 72 dwords, conflict-free transposing reads
 constexpr float kPNegBig = -1.0e30f;
 constexpr float kPRescale = 8.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct PrefillSmem {
   uint16_t k[2][kKeys][kKStride];     // K tile, [key][d]
-  uint16_t vt[2][kD][kVStride];       // V tile transposed, [d][key]
+  uint16_t v[2][kKeys][kVStride];     // V tile, [key][d]
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -115,51 +124,59 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * kD * 2;
   const uint32_t block_bytes = row_bytes * kBlockSize;
 
-  // ---- K/V tile loader: 64 keys x 128 d, K as [key][d], V as [d][key] --------
-  // thread -> (key pair kp = tid / 16 * 2 .. +1, d chunk dc = tid % 16)
-  const int ld_key = (tid >> 4) * 2;  // 0, 2, ..., 30 (+32 for the second pass)
-  const int ld_dc = tid & 15;         // 8-element chunk of d
-  uint4 kreg[2][2], vreg[2][2];       // [pass][key of the pair]
-  auto fetch = [&](int kt) {
+  // ---- K/V tile loader: 64 keys x 128 d, K and V as [key][d] rows -----------
+  // thread -> (key pair 8 w + 2 (lane / 16) (+32 for the second pass), d chunk
+  // dc = lane % 16): the keys of one wave and pass lie in one 16-token block,
+  // so its block id is wave-uniform and the loads go through a buffer
+  // descriptor; keys past the context read as zeros (offset past the
+  // descriptor's size), so no pool row outside the context reaches the P.V
+  const int ld_key = 8 * wave + 2 * (lane >> 4);   // 0, 2, ..., 30
+  const int ld_dc = lane & 15;                      // 8-element chunk of d
+  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + (g * kD + ld_dc * 8) * 2;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  auto load_ids = [&](int kt, int (&ids)[2]) {
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
+      const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;   // the wave's first key this pass
+      ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
+    }
+  };
+  uint4 kreg[2][2], vreg[2][2];       // [pass][key of the pair]
+  auto fetch = [&](int kt, const int (&ids)[2]) {
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const int phys = uniform(ids[ps]);
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      const int64_t boff = ok ? static_cast<int64_t>(phys) * block_bytes : 0;
+      const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
+      const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int key = ld_key + 32 * ps + e;
-        const int kpos = kt * kKeys + key;
-        uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
-        if (kpos < L) {
-          const int phys = table[kpos / kBlockSize];
-          if (phys >= 0 && phys < a.num_blocks) {
-            const int64_t off = static_cast<int64_t>(phys) * block_bytes +
-                                (kpos % kBlockSize) * row_bytes + (g * kD + ld_dc * 8) * 2;
-            kx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_cache) + off);
-            vx = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_cache) + off);
-          }
-        }
-        kreg[ps][e] = kx;
-        vreg[ps][e] = vx;
+        const int kpos = kt * kKeys + ld_key + 32 * ps + e;
+        const uint32_t off = kpos < L ? ld_off + e * row_bytes : block_bytes;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        kreg[ps][e] = make_uint4(kx[0], kx[1], kx[2], kx[3]);
+        vreg[ps][e] = make_uint4(vx[0], vx[1], vx[2], vx[3]);
       }
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
+    for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        *reinterpret_cast<uint4*>(&sm.k[buf][ld_key + 32 * ps + e][ld_dc * 8]) = kreg[ps][e];
-      // V^T: pair the two keys' values of each d into one dword
-      const uint32_t* va = reinterpret_cast<const uint32_t*>(&vreg[ps][0]);
-      const uint32_t* vb = reinterpret_cast<const uint32_t*>(&vreg[ps][1]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = ld_dc * 8 + 2 * w;
-        const int key = ld_key + 32 * ps;
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d][key]) = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d + 1][key]) = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
+      for (int e = 0; e < 2; ++e) {
+        const int key = ld_key + 32 * ps + e;
+        *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 8]) = kreg[ps][e];
+        *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 8]) = vreg[ps][e];
       }
-    }
   };
+  // transposing-read source address of this lane: key row 4 * half + (lane % 16) / 4,
+  // d column 16 * (lane / 16 mod 2) + 4 * (lane mod 4) (plus the step's offsets)
+  const int tr_row = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 o[kD / 32];                  // O^T: 4 d-tiles of 32 x (32 columns)
 #pragma unroll
@@ -168,78 +185,87 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m = kPNegBig, lsum = 0.f;
   const float sl2 = a.scale_log2;
+  // the tile's smallest query position: key tiles up to it need no mask
+  const int min_qpos = first_pos + t0;
 
+  int ids[2];
   if (n_kt > 0) {
-    fetch(0);
+    load_ids(0, ids);
+    fetch(0, ids);
+    if (n_kt > 1) load_ids(1, ids);
     stash(0);
   }
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) fetch(kt + 1);   // next tile's loads fly during this tile's math
+    if (kt + 1 < n_kt) {
+      fetch(kt + 1, ids);               // next tile's loads fly during this tile's math
+      if (kt + 2 < n_kt) load_ids(kt + 2, ids);
+    }
 
-    // ---- S^T = K . Q^T for the two 32-key halves of the tile ---------------
-    f32x16 st[2];
+    // ---- per 32-key half: S^T = K . Q^T, softmax, O^T += V^T . P^T ----------
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      f32x16 st;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
         const uint4 kx = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * t + col][16 * kk + 8 * half]);
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
-                                                         st[t], 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk], st,
+                                                      0, 0, 0);
       }
-    }
-    // ---- scale, causal mask, online softmax per column ---------------------
-    float tmax = kPNegBig;
+      // causal mask only where the half reaches past a position; lanes of
+      // invalid columns compute values that are never stored
+      const int key0 = kt * kKeys + 32 * t;
+      if (key0 + 31 > min_qpos) {
+        const int lim = qpos - key0 - 4 * half;   // r-part of the key offset must not exceed it
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * kKeys + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float z = (col_valid && key <= qpos) ? st[t][r] * sl2 : -INFINITY;
-        st[t][r] = z;
-        tmax = fmaxf(tmax, z);
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kPRescale) != 0) {
-      const float m_new = tmax > m + kPRescale ? tmax : m;
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lsum *= alpha;
+      float tmax = st[0];
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;
+      if (__builtin_amdgcn_ballot_w64(tmax > m + kPRescale) != 0) {
+        const float m_new = tmax > m + kPRescale ? tmax : m;
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    // P^T in bf16, packed straight from the accumulator layout
-    uint32_t pk[2][8];
+        for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      // P^T in bf16, packed straight from the accumulator layout
+      uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(st[t][r] - m);
-        const float p1 = fast_exp2(st[t][r + 1] - m);
+        const float p0 = fast_exp2(fmaf(st[r], sl2, -m));
+        const float p1 = fast_exp2(fmaf(st[r + 1], sl2, -m));
         lsum += p0 + p1;
-        pk[t][r >> 1] = pack_bf16(p0, p1);
+        pk[r >> 1] = pack_bf16(p0, p1);
       }
-    // ---- O^T += V^T . P^T over four 16-key steps -----------------------------
 #pragma unroll
-    for (int cstep = 0; cstep < kKeys / 16; ++cstep) {
-      const int t = cstep >> 1;
-      const int rb = (cstep & 1) * 4;   // dwords of pk[t] for this step
-      const uint4 pb = make_uint4(pk[t][rb], pk[t][rb + 1], pk[t][rb + 2], pk[t][rb + 3]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
-      const int key_a = 16 * cstep + 4 * half;     // keys key_a..+3 and key_a+8..+11
+      for (int ch = 0; ch < 2; ++ch) {
+        const int cstep = 2 * t + ch;   // 16-key step of the tile
+        const bf16x8 pf = __builtin_bit_cast(
+            bf16x8, make_uint4(pk[4 * ch], pk[4 * ch + 1], pk[4 * ch + 2], pk[4 * ch + 3]));
+        // keys 16c + 4 half + 0..3 and + 8..11 of d column 32 dt + lane % 32
+        const int row = 16 * cstep + tr_row;
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
-        const int d = 32 * dt + col;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&sm.vt[buf][d][key_a]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&sm.vt[buf][d][key_a + 8]);
-        const uint4 vx = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vx), pf, o[dt],
-                                                         0, 0, 0);
+        for (int dt = 0; dt < kD / 32; ++dt) {
+          const int dcol = 32 * dt + tr_col;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)&sm.v[buf][row][dcol]);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)&sm.v[buf][row + 8][dcol]);
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8 vx = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx, pf, o[dt], 0, 0, 0);
+        }
       }
     }
     // buffer buf^1 was last read in the previous tile, before its barrier
