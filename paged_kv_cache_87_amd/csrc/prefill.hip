@@ -63,6 +63,13 @@ struct PrefillSmem {
   uint16_t v[2][kKeys][kVStride];     // V tile, [key][d]
 };
 
+// x of lane ^ 32 through the gfx950 lane-half swap (no LDS round trip)
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2 two = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
@@ -203,18 +210,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       if (kt + 2 < n_kt) load_ids(kt + 2, ids);
     }
 
-    // ---- per 32-key half: S^T = K . Q^T, softmax, O^T += V^T . P^T ----------
+    // ---- S^T = K . Q^T for both 32-key halves first, so the second half's
+    // matrix work runs while the first half's softmax is on the VALU ---------
+    f32x16 st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f32x16 st;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
         const uint4 kx = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * t + col][16 * kk + 8 * half]);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk], st,
-                                                      0, 0, 0);
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
+                                                         st[t], 0, 0, 0);
       }
+    }
+    // ---- per half: causal mask, online softmax, O^T += V^T . P^T ------------
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       // causal mask only where the half reaches past a position; lanes of
       // invalid columns compute values that are never stored
       const int key0 = kt * kKeys + 32 * t;
@@ -222,12 +234,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         const int lim = qpos - key0 - 4 * half;   // r-part of the key offset must not exceed it
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
+          if (8 * (r >> 2) + (r & 3) > lim) st[t][r] = -INFINITY;
       }
-      float tmax = st[0];
+      float tmax = st[t][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, st[t][r]);
+      tmax = fmaxf(tmax, xor32(tmax)) * sl2;
       if (__builtin_amdgcn_ballot_w64(tmax > m + kPRescale) != 0) {
         const float m_new = tmax > m + kPRescale ? tmax : m;
         const float alpha = fast_exp2(m - m_new);
@@ -242,8 +254,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(st[r], sl2, -m));
-        const float p1 = fast_exp2(fmaf(st[r + 1], sl2, -m));
+        const float p0 = fast_exp2(fmaf(st[t][r], sl2, -m));
+        const float p1 = fast_exp2(fmaf(st[t][r + 1], sl2, -m));
         lsum += p0 + p1;
         pk[r >> 1] = pack_bf16(p0, p1);
       }
@@ -274,7 +286,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- normalise and store: lane holds column `col`, rows d ----------------
-  lsum += __shfl_xor(lsum, 32);
+  lsum += xor32(lsum);
   if (!col_valid) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(a.out) +
