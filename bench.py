@@ -12,8 +12,8 @@ Printed: one JSON line with whole-step throughput (K/V bytes read per
 second), the decode call's roofline (K/V bytes / decode kernel time against
 8 TB/s, timed with events over the timed region), the CPU oracle timed on a
 bounded sample of the same workload, and secondary measurements of the
-batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16) and of the
-long-context shared-prefix decode.
+batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16), of the
+long-context shared-prefix decode and of the copy-on-write block copy.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
@@ -191,6 +191,27 @@ def secondary(torch, np, stream, K, W):
         "unique_kv_GBps": unique / (dec * 1e-3) / 1e9,
         "frac_hbm_peak_unique": unique / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS,
     }
+    del g
+    torch.cuda.empty_cache()
+    # copy-on-write data move: 2048 disjoint block pairs of a 40000-block
+    # 8 x 128 bf16 pool (32 KiB per block and pool), K and V
+    from paged_kv_cache_87_amd import binding
+    nb, pairs = 40000, 2048
+    kc = torch.zeros((nb, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    pool = binding.KVPool(kc, vc)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(87005))
+    src = perm[:pairs].to(torch.int32).cuda()
+    dst = perm[pairs:2 * pairs].to(torch.int32).cuda()
+    _, cp_ms = timed(torch, stream, K, W, lambda: None,
+                     lambda: binding.pa_copy_blocks(pool, src, dst))
+    cp = float(np.mean(cp_ms))
+    moved = 2 * 2 * pairs * 16 * 8 * 128 * 2          # read + write, K and V
+    out["cow_copy_blocks"] = {
+        "config": {"pairs": pairs, "block_bytes_per_pool": 16 * 8 * 128 * 2},
+        "copy_us": cp * 1e3, "hbm_GBps": moved / (cp * 1e-3) / 1e9,
+        "frac_hbm_peak": moved / (cp * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+    }
     return out
 
 
@@ -244,7 +265,7 @@ def main():
     del g
     torch.cuda.empty_cache()
 
-    sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 3)
+    sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 30)
     cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
 
     traffic = measured_traffic(w.name, args.partition_size)

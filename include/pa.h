@@ -25,8 +25,10 @@
  *   bfloat16 (the high 16 bits of a binary32).  q, out, k_new and v_new use
  *   the pool's element type.
  * - The library keeps no state between calls apart from thread-local error
- *   text, so calls from several host threads are safe.  Calls that write
- *   the same device memory must be ordered by the caller (one stream).
+ *   text and the block allocators the caller creates, so calls from several
+ *   host threads are safe; one allocator must not be used by two threads at
+ *   once.  Calls that write the same device memory must be ordered by the
+ *   caller (one stream).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -46,7 +48,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer ... */
   PA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels cover  */
   PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required    */
-  PA_ERR_HIP = -4           /* the HIP runtime refused a launch              */
+  PA_ERR_HIP = -4,          /* the HIP runtime refused a launch              */
+  PA_ERR_NO_BLOCKS = -5     /* the block allocator has too few free blocks   */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -138,6 +141,75 @@ pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
 pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                       const int64_t* slot_mapping, int32_t num_tokens,
                       hipStream_t stream);
+
+/*
+ * Copy-on-write paging (JuliaPagedAttn README, "Copy-on-Write": sequences
+ * that share a prefix name the same physical blocks, whose reference count
+ * is then above one; a write into such a block first allocates a new block,
+ * copies the data, points the writer's table at the copy and drops one
+ * reference from the shared block).
+ *
+ * pa_block_allocator -- host-side free list and reference counts of one
+ * pool's num_blocks physical blocks.  Free ids are handed out first-in
+ * first-out: 0 .. num_blocks-1 in order at first, released ids appended at
+ * the back (Pico-vLLM #5 Paged Attention, "核心数据结构和设计模式",
+ * BlockManager: deque of free ids, popleft / append).  Every call checks
+ * its whole request first; a failed call changes nothing.  Host memory
+ * only; an allocator is not thread-safe.
+ */
+typedef struct pa_block_allocator pa_block_allocator;
+
+/* A new allocator with every block free; *out receives it. */
+pa_status pa_allocator_create(int32_t num_blocks, pa_block_allocator** out);
+void pa_allocator_destroy(pa_block_allocator* alloc);
+/* Free blocks now (-1 for a null allocator). */
+int32_t pa_allocator_num_free(const pa_block_allocator* alloc);
+/* References held on `block` (0 = free; -1 = not a block of the pool). */
+int32_t pa_allocator_refcount(const pa_block_allocator* alloc, int32_t block);
+
+/* Take n free blocks into blocks[0..n) (host), each with one reference.
+ * PA_ERR_NO_BLOCKS if fewer than n are free (the p2 allocate error). */
+pa_status pa_allocator_allocate(pa_block_allocator* alloc, int32_t n, int32_t* blocks);
+
+/* One more reference on each listed block: another table now names it
+ * (JuliaPagedAttn's cow_fork!).  Every block must be allocated. */
+pa_status pa_allocator_fork(pa_block_allocator* alloc, const int32_t* blocks, int32_t n);
+
+/* Drop one reference per listing; a block whose count reaches 0 goes to
+ * the back of the free list, in listing order.  A block listed k times must
+ * hold at least k references. */
+pa_status pa_allocator_release(pa_block_allocator* alloc, const int32_t* blocks, int32_t n);
+
+/*
+ * pa_allocator_prepare_write -- make positions [start, start+count) of one
+ * sequence writable before its K/V are written there.
+ *
+ * table (host, int32 [width]) is the sequence's block-table row, of which
+ * entries [0, *num_used) are in use.  Every touched entry that names a
+ * shared block (reference count > 1) is replaced by a freshly allocated
+ * block: the pair (old, new) is appended to copy_src / copy_dst (host,
+ * capacity copy_cap; *num_copies receives the count) and one reference is
+ * dropped from the old block.  Touched entries at or past *num_used are
+ * filled with freshly allocated blocks and *num_used grows.  The caller then
+ * uploads the row, runs pa_copy_blocks on the pairs and writes the K/V.
+ * start must not leave a gap (start <= *num_used * block_size).
+ * PA_ERR_NO_BLOCKS if the allocator cannot supply every block needed.
+ */
+pa_status pa_allocator_prepare_write(pa_block_allocator* alloc, int32_t* table, int32_t width,
+                                     int32_t* num_used, int32_t block_size, int32_t start,
+                                     int32_t count, int32_t* copy_src, int32_t* copy_dst,
+                                     int32_t copy_cap, int32_t* num_copies);
+
+/*
+ * pa_copy_blocks -- copy whole blocks of both pools on the device: for each
+ * pair i, block src_blocks[i] of k_cache and of v_cache is copied bit for
+ * bit to block dst_blocks[i] (the data move of a copy-on-write).
+ * src_blocks / dst_blocks: device int32 [num_pairs]; pairs naming a block
+ * outside the pool are skipped.  A destination that is also a source, or
+ * listed twice, races (the caller's responsibility).  num_pairs <= 65535.
+ */
+pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t num_pairs, hipStream_t stream);
 
 /*
  * pa_decode_workspace_bytes -- device workspace pa_decode needs for this

@@ -24,12 +24,16 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_NO_BLOCKS = -5
 PA_F32 = 0
 PA_BF16 = 1
 
 EXPORTED = (
     "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill",
-    "pa_status_string", "pa_last_error", "pa_version",
+    "pa_status_string", "pa_last_error", "pa_version", "pa_allocator_create",
+    "pa_allocator_destroy", "pa_allocator_num_free", "pa_allocator_refcount",
+    "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
+    "pa_allocator_prepare_write", "pa_copy_blocks",
 )
 
 
@@ -83,6 +87,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_status_string": (ctypes.c_char_p, [i32]),
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_version": (i32, []),
+        "pa_allocator_create": (i32, [i32, ctypes.POINTER(vp)]),
+        "pa_allocator_destroy": (None, [vp]),
+        "pa_allocator_num_free": (i32, [vp]),
+        "pa_allocator_refcount": (i32, [vp, i32]),
+        "pa_allocator_allocate": (i32, [vp, i32, vp]),
+        "pa_allocator_fork": (i32, [vp, vp, i32]),
+        "pa_allocator_release": (i32, [vp, vp, i32]),
+        "pa_allocator_prepare_write": (i32, [vp, vp, i32, vp, i32, i32, i32, vp, vp, i32, vp]),
+        "pa_copy_blocks": (i32, [pool_p, vp, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -248,6 +261,82 @@ def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
     return out
 
 
+def _i32_array(values):
+    arr = (ctypes.c_int32 * max(1, len(values)))(*[int(v) for v in values])
+    return arr
+
+
+class BlockAllocator:
+    """The library's host-side refcounted block allocator (first-in
+    first-out free list), one per pool.  Lists in and out are Python ints."""
+
+    def __init__(self, num_blocks: int):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check("pa_allocator_create", lib.pa_allocator_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def close(self):
+        if self._h:
+            load_library().pa_allocator_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(load_library().pa_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(load_library().pa_allocator_refcount(self._h, int(block)))
+
+    def allocate(self, n: int) -> list:
+        out = (ctypes.c_int32 * max(1, n))()
+        _check("pa_allocator_allocate", load_library().pa_allocator_allocate(self._h, int(n), out))
+        return [int(out[i]) for i in range(n)]
+
+    def fork(self, blocks) -> None:
+        arr = _i32_array(blocks)
+        _check("pa_allocator_fork", load_library().pa_allocator_fork(self._h, arr, len(blocks)))
+
+    def release(self, blocks) -> None:
+        arr = _i32_array(blocks)
+        _check("pa_allocator_release",
+               load_library().pa_allocator_release(self._h, arr, len(blocks)))
+
+    def prepare_write(self, table: list, num_used: int, block_size: int, start: int,
+                      count: int, width: int = None):
+        """Returns (new table row, new num_used, [(src, dst) copies]); the
+        row is a list of `width` ints (entries past num_used are ignored)."""
+        width = len(table) if width is None else width
+        row = _i32_array(list(table) + [-1] * (width - len(table)))
+        used = ctypes.c_int32(int(num_used))
+        cap = width
+        src = (ctypes.c_int32 * cap)()
+        dst = (ctypes.c_int32 * cap)()
+        nc = ctypes.c_int32(0)
+        _check("pa_allocator_prepare_write", load_library().pa_allocator_prepare_write(
+            self._h, row, int(width), ctypes.byref(used), int(block_size), int(start),
+            int(count), src, dst, cap, ctypes.byref(nc)))
+        return ([int(row[i]) for i in range(width)], int(used.value),
+                [(int(src[i]), int(dst[i])) for i in range(nc.value)])
+
+
+def pa_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D of the same length")
+    n = int(src.shape[0])
+    cp = pool.c()
+    st = load_library().pa_copy_blocks(ctypes.byref(cp), _dev(src, "src", torch.int32),
+                                       _dev(dst, "dst", torch.int32), n, _stream(stream))
+    _check("pa_copy_blocks", st)
+
+
 def pa_version() -> int:
     return int(load_library().pa_version())
 
@@ -255,6 +344,7 @@ def pa_version() -> int:
 __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
-    "decode_workspace", "pa_decode", "pa_prefill", "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
-    "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_F32", "PA_BF16",
+    "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
+    "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
+    "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_BLOCKS", "PA_F32", "PA_BF16",
 ]

@@ -93,6 +93,17 @@ int32_t context_cap(const pa_seq_desc* seqs) {
 }  // namespace
 
 namespace pa {
+void clear_report() { clear_error(); }
+pa_status report(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace pa
+
+namespace pa {
 
 hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out) {
   static std::mutex mu;
@@ -155,6 +166,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS";
     default: return "PA_ERR_UNKNOWN";
   }
 }
@@ -197,6 +209,24 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
                     pool->num_kv_heads * pool->head_dim * elt_size(pool->dtype),
                     static_cast<int64_t>(pool->num_blocks) * pool->block_size};
   return hip_status(pa::launch_write_kv(a, stream), "write_kv launch");
+}
+
+pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t num_pairs, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "src_blocks or dst_blocks is null");
+  if (num_pairs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_pairs %d (at most 65535 a call)", num_pairs);
+  pa::CopyBlocksArgs a{pool->k_cache, pool->v_cache, src_blocks, dst_blocks, num_pairs,
+                       pool->num_blocks,
+                       static_cast<int64_t>(pool->block_size) * pool->num_kv_heads *
+                           pool->head_dim * elt_size(pool->dtype)};
+  return hip_status(pa::launch_copy_blocks(a, stream), "copy_blocks launch");
 }
 
 size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs,

@@ -6,7 +6,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Thread-local error text behind pa_last_error(): clear at entry, set with
+// the failing status (returned unchanged).
+void clear_report();
+pa_status report(pa_status status, const char* fmt, ...);
 
 constexpr int kBlockSize = 16;  // tokens per physical block the kernels handle
 
@@ -33,6 +40,17 @@ struct WriteKVArgs {
   int64_t num_slots;       // num_blocks * block_size
 };
 hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream);
+
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;      // [num_pairs] source block ids
+  const int32_t* dst;      // [num_pairs] destination block ids
+  int32_t num_pairs;
+  int32_t num_blocks;
+  int64_t block_bytes;     // block_size * num_kv_heads * head_dim * element size (multiple of 64)
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;

@@ -126,3 +126,34 @@ def test_prefill_unsupported_shapes_rejected():
     with pytest.raises(pa.PagedAttentionError) as e:
         g.attend()
     assert e.value.status == pa.PA_ERR_UNSUPPORTED
+
+
+def test_mixed_decode_and_prefill_batch():
+    """A continuous-batching step in one pa_prefill call: decode sequences
+    (one new token at the end of a long history) next to chunked and whole
+    prompts.  Every output row against the oracle; each decode row also
+    through pa_decode over the same pool, against the same oracle rows."""
+    lens = [1500, 40, 700, 2049, 1, 333, 96, 4100]
+    q_lens = [1, 40, 1, 300, 1, 333, 17, 1]
+    w = wl.prefill_workload("mixed_batch", 640, dtype=wl.BF16, num_q_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=16, num_blocks=1024, context_lens=lens,
+                            q_lens=q_lens)
+    announce(w.name)
+    g = _run(w)
+    k_ref, v_ref, slots_ref, out_ref = orun.run_step(w)
+    assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
+    assert_pools_equal(g, k_ref, v_ref)
+    assert_close(g.out_f64(), out_ref, w.dtype, w.name)
+    dec = [s for s in range(w.num_seqs) if q_lens[s] == 1]
+    rows = [int(w.q_start_loc[s]) for s in dec]
+    idx = torch.tensor(dec, dtype=torch.long, device="cuda")
+    seqs = pa.SeqDesc(g.block_tables.index_select(0, idx).contiguous(),
+                      g.context_lens.index_select(0, idx).contiguous(), max(lens))
+    q = g.q[rows].contiguous()
+    out = torch.empty_like(q)
+    for part in (0, 512):
+        ws = pa.decode_workspace(g.pool, seqs, w.num_q_heads, part) if part else None
+        pa.pa_decode(g.pool, seqs, q, out, w.scale, part, ws)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().numpy().astype(np.float64), out_ref[rows], w.dtype,
+                     f"decode rows, partition {part}")
