@@ -13,7 +13,8 @@ second), the decode call's roofline (K/V bytes / decode kernel time against
 8 TB/s, timed with events over the timed region), the CPU oracle timed on a
 bounded sample of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16), of the
-long-context shared-prefix decode and of the copy-on-write block copy.
+long-context shared-prefix decode, of the copy-on-write block copy and of
+the block swap between the device pool and a pinned host pool.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PCIE5_X16_GBPS = 63.0   # 32 GT/s x 16 lanes, 128b/130b coding, one direction
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode μs/step + KV-read HBM GB/s (% of peak), batch 64 ctx 4096"
@@ -212,6 +214,33 @@ def secondary(torch, np, stream, K, W):
         "copy_us": cp * 1e3, "hbm_GBps": moved / (cp * 1e-3) / 1e9,
         "frac_hbm_peak": moved / (cp * 1e-3) / 1e9 / HBM_PEAK_GBPS,
     }
+    # offload tier: the same 2048 blocks swapped out to a pinned host pool and
+    # back, against a plain contiguous host<->device copy of the same bytes
+    hk = torch.zeros((4096, 16, 8, 128), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    hsl = torch.randperm(4096, generator=torch.Generator().manual_seed(87006))[:pairs]
+    hsl = hsl.to(torch.int32).cuda()
+    _, out_ms = timed(torch, stream, K, W, lambda: None, lambda: binding.pa_swap_blocks(
+        pool, hk, hv, src, hsl, binding.PA_SWAP_OUT))
+    _, in_ms = timed(torch, stream, K, W, lambda: None, lambda: binding.pa_swap_blocks(
+        pool, hk, hv, dst, hsl, binding.PA_SWAP_IN))
+    link = 2 * pairs * 16 * 8 * 128 * 2                # K and V, one way
+    flat_h = hk.view(-1)[:link // 2]
+    flat_d = kc.view(-1)[:link // 2]
+    _, d2h_ms = timed(torch, stream, K, W, lambda: None,
+                      lambda: flat_h.copy_(flat_d, non_blocking=True))
+    _, h2d_ms = timed(torch, stream, K, W, lambda: None,
+                      lambda: flat_d.copy_(flat_h, non_blocking=True))
+    gbps = lambda ms, b: b / (float(np.mean(ms)) * 1e-3) / 1e9  # noqa: E731
+    out["swap_blocks"] = {
+        "config": {"pairs": pairs, "bytes_each_way": link, "host_pool_blocks": 4096},
+        "swap_out_us": float(np.mean(out_ms)) * 1e3, "swap_in_us": float(np.mean(in_ms)) * 1e3,
+        "swap_out_GBps": gbps(out_ms, link), "swap_in_GBps": gbps(in_ms, link),
+        "contiguous_d2h_GBps": gbps(d2h_ms, link // 2),
+        "contiguous_h2d_GBps": gbps(h2d_ms, link // 2),
+        "pcie5_x16_peak_GBps": PCIE5_X16_GBPS,
+    }
+    del hk, hv
     return out
 
 

@@ -212,6 +212,41 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
                          const int32_t* dst_blocks, int32_t num_pairs, hipStream_t stream);
 
 /*
+ * pa_swap_blocks -- move whole blocks between the device pool and a pool in
+ * pinned host memory (Pico-vLLM #5 Paged Attention, BlockManager swap_out:
+ * a GPU block is copied into a free CPU block of the pinned CPU pool;
+ * swap_in: back into a free GPU block).  Pair i copies, in both K and V,
+ * device block device_blocks[i] to host block host_blocks[i]
+ * (direction PA_SWAP_OUT) or host block host_blocks[i] to device block
+ * device_blocks[i] (PA_SWAP_IN), bit for bit.  The caller does the
+ * bookkeeping (which blocks are free; pa_block_allocator serves either pool).
+ *
+ * host_pool: k_cache / v_cache in pinned host memory (hipHostMalloc, or a
+ * pinned torch tensor), same block_size, num_kv_heads, head_dim and dtype as
+ * device_pool; the device reads or writes it directly, so one launch moves
+ * the whole batch.  device_blocks / host_blocks: int32 [num_pairs] readable by
+ * the device (device memory or pinned host memory).  Pairs naming a block
+ * outside its pool are skipped.  The copy is asynchronous on `stream`: the
+ * host pool may be read, or reused, after the stream has passed it.
+ * The library owns nothing; both pools and both id arrays stay the caller's.
+ *
+ * Errors (nothing enqueued): PA_ERR_INVALID_ARG for a bad descriptor, pools
+ * whose block shape or dtype differ, an unknown direction, a device pool that
+ * is not device memory, a host pool that is not pinned host memory mapped to
+ * the device at the same address (pageable memory is refused, since the
+ * kernel would fault on it), or id arrays the device cannot read;
+ * PA_ERR_UNSUPPORTED for num_pairs > 65535; PA_ERR_HIP if the launch fails.
+ */
+typedef enum pa_swap_direction {
+  PA_SWAP_OUT = 0,  /* device pool -> host pool */
+  PA_SWAP_IN = 1    /* host pool -> device pool */
+} pa_swap_direction;
+
+pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_pool,
+                         const int32_t* device_blocks, const int32_t* host_blocks,
+                         int32_t num_pairs, int32_t direction, hipStream_t stream);
+
+/*
  * pa_decode_workspace_bytes -- device workspace pa_decode needs for this
  * pool, batch shape, num_q_heads and partition_size (only the pool's sizes
  * are read, not its pointers).

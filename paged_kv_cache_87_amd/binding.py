@@ -27,13 +27,15 @@ PA_ERR_HIP = -4
 PA_ERR_NO_BLOCKS = -5
 PA_F32 = 0
 PA_BF16 = 1
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
 
 EXPORTED = (
     "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill",
     "pa_status_string", "pa_last_error", "pa_version", "pa_allocator_create",
     "pa_allocator_destroy", "pa_allocator_num_free", "pa_allocator_refcount",
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
-    "pa_allocator_prepare_write", "pa_copy_blocks",
+    "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks",
 )
 
 
@@ -96,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_allocator_release": (i32, [vp, vp, i32]),
         "pa_allocator_prepare_write": (i32, [vp, vp, i32, vp, i32, i32, i32, vp, vp, i32, vp]),
         "pa_copy_blocks": (i32, [pool_p, vp, vp, i32, vp]),
+        "pa_swap_blocks": (i32, [pool_p, pool_p, vp, vp, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -337,6 +340,32 @@ def pa_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=No
     _check("pa_copy_blocks", st)
 
 
+def host_pool_c(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaKVPool:
+    """Descriptor of a K/V pool held in pinned host memory (``pin_memory=True``
+    tensors, ``[num_blocks, block_size, num_kv_heads, head_dim]`` each)."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous pinned host tensor")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
+        raise ValueError("host k_cache and v_cache must be [N, block_size, Hkv, D] alike")
+    N, B, H, D = k_cache.shape
+    return PaKVPool(k_cache.data_ptr(), v_cache.data_ptr(), N, B, H, D,
+                    _dtype_code(k_cache.dtype))
+
+
+def pa_swap_blocks(pool: KVPool, host_k: torch.Tensor, host_v: torch.Tensor,
+                   device_blocks: torch.Tensor, host_blocks: torch.Tensor, direction: int,
+                   stream=None) -> None:
+    if device_blocks.shape != host_blocks.shape or device_blocks.dim() != 1:
+        raise ValueError("device_blocks and host_blocks must be 1-D of the same length")
+    cp, ch = pool.c(), host_pool_c(host_k, host_v)
+    st = load_library().pa_swap_blocks(
+        ctypes.byref(cp), ctypes.byref(ch), _dev(device_blocks, "device_blocks", torch.int32),
+        _dev(host_blocks, "host_blocks", torch.int32), int(device_blocks.shape[0]),
+        int(direction), _stream(stream))
+    _check("pa_swap_blocks", st)
+
+
 def pa_version() -> int:
     return int(load_library().pa_version())
 
@@ -345,6 +374,7 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
     "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
+    "host_pool_c", "pa_swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
     "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
     "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_BLOCKS", "PA_F32", "PA_BF16",
 ]

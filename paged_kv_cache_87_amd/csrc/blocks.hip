@@ -7,6 +7,12 @@
 // grid (pair, pool, quarter of the block), 256 threads; each thread moves
 // 16-byte chunks with a stride of one workgroup.  Pairs whose ids are outside
 // the pool are skipped.
+//
+// The same kernel moves blocks between the device pool and a pool in pinned
+// host memory (Pico-vLLM #5 Paged Attention, BlockManager swap_out /
+// swap_in: a GPU block is copied into a CPU block of the pinned CPU pool and
+// back): the device reads or writes the host pool directly through its
+// mapping, so a whole batch of blocks is one launch.
 
 #include "pa_internal.h"
 
@@ -21,9 +27,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
   const int p = blockIdx.x;
   const int src = a.src[p];
   const int dst = a.dst[p];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  const char* base = static_cast<const char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
-  char* out = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) return;
+  const char* base = static_cast<const char*>(blockIdx.y == 0 ? a.src_k : a.src_v);
+  char* out = static_cast<char*>(blockIdx.y == 0 ? a.dst_k : a.dst_v);
   const int64_t chunks = a.block_bytes >> 4;          // 16-byte chunks per block
   const int64_t per = chunks / kCopySplit;
   const int64_t c0 = per * blockIdx.z;

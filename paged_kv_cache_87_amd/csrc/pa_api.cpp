@@ -85,6 +85,25 @@ pa_status check_heads(const pa_kv_pool* pool, int32_t num_q_heads) {
   return PA_OK;
 }
 
+// True when [p, p + bytes) starts and ends in memory the current device can
+// address at the same pointer: pinned host memory (hipHostMalloc) when
+// `host`, device memory otherwise.  A kernel that touched pageable or
+// unmapped memory would fault, so the swap checks its arguments with this
+// before anything is enqueued.
+bool device_addressable(const void* p, size_t bytes, bool host) {
+  const char* c = static_cast<const char*>(p);
+  for (const char* q : {c, c + bytes - 1}) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, q) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (at.type != (host ? hipMemoryTypeHost : hipMemoryTypeDevice)) return false;
+    if (at.devicePointer != q) return false;
+  }
+  return true;
+}
+
 int32_t context_cap(const pa_seq_desc* seqs) {
   const int64_t by_table = static_cast<int64_t>(seqs->max_blocks_per_seq) * pa::kBlockSize;
   return static_cast<int32_t>(seqs->max_context_len < by_table ? seqs->max_context_len : by_table);
@@ -222,11 +241,53 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
     return fail(PA_ERR_INVALID_ARG, "src_blocks or dst_blocks is null");
   if (num_pairs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "num_pairs %d (at most 65535 a call)", num_pairs);
-  pa::CopyBlocksArgs a{pool->k_cache, pool->v_cache, src_blocks, dst_blocks, num_pairs,
-                       pool->num_blocks,
+  pa::CopyBlocksArgs a{pool->k_cache, pool->v_cache, pool->k_cache, pool->v_cache,
+                       src_blocks, dst_blocks, num_pairs, pool->num_blocks, pool->num_blocks,
                        static_cast<int64_t>(pool->block_size) * pool->num_kv_heads *
                            pool->head_dim * elt_size(pool->dtype)};
   return hip_status(pa::launch_copy_blocks(a, stream), "copy_blocks launch");
+}
+
+pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_pool,
+                         const int32_t* device_blocks, const int32_t* host_blocks,
+                         int32_t num_pairs, int32_t direction, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(device_pool);
+  if (st != PA_OK) return st;
+  if ((st = check_pool(host_pool)) != PA_OK) return st;
+  if (host_pool->block_size != device_pool->block_size ||
+      host_pool->num_kv_heads != device_pool->num_kv_heads ||
+      host_pool->head_dim != device_pool->head_dim || host_pool->dtype != device_pool->dtype)
+    return fail(PA_ERR_INVALID_ARG, "host and device pools differ in block shape or dtype");
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID_ARG, "direction %d", direction);
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (device_blocks == nullptr || host_blocks == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "device_blocks or host_blocks is null");
+  if (num_pairs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "num_pairs %d (at most 65535 a call)", num_pairs);
+  const int64_t bb = static_cast<int64_t>(device_pool->block_size) * device_pool->num_kv_heads *
+                     device_pool->head_dim * elt_size(device_pool->dtype);
+  const size_t ids = sizeof(int32_t) * static_cast<size_t>(num_pairs);
+  for (const void* p : {device_pool->k_cache, device_pool->v_cache})
+    if (!device_addressable(p, bb * device_pool->num_blocks, false))
+      return fail(PA_ERR_INVALID_ARG, "device pool is not device memory of the current device");
+  for (const void* p : {host_pool->k_cache, host_pool->v_cache})
+    if (!device_addressable(p, bb * host_pool->num_blocks, true))
+      return fail(PA_ERR_INVALID_ARG,
+                  "host pool is not pinned host memory mapped at the same address");
+  for (const void* p : {static_cast<const void*>(device_blocks),
+                        static_cast<const void*>(host_blocks)})
+    if (!device_addressable(p, ids, false) && !device_addressable(p, ids, true))
+      return fail(PA_ERR_INVALID_ARG, "block id arrays must be device or pinned host memory");
+  const bool out = direction == PA_SWAP_OUT;
+  const pa_kv_pool* s = out ? device_pool : host_pool;
+  const pa_kv_pool* d = out ? host_pool : device_pool;
+  pa::CopyBlocksArgs a{s->k_cache, s->v_cache, d->k_cache, d->v_cache,
+                       out ? device_blocks : host_blocks, out ? host_blocks : device_blocks,
+                       num_pairs, s->num_blocks, d->num_blocks, bb};
+  return hip_status(pa::launch_copy_blocks(a, stream), "swap_blocks launch");
 }
 
 size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs,

@@ -42,12 +42,15 @@ struct WriteKVArgs {
 hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream);
 
 struct CopyBlocksArgs {
-  void* k_cache;
-  void* v_cache;
+  const void* src_k;       // source pools (device or pinned host)
+  const void* src_v;
+  void* dst_k;             // destination pools (device or pinned host)
+  void* dst_v;
   const int32_t* src;      // [num_pairs] source block ids
   const int32_t* dst;      // [num_pairs] destination block ids
   int32_t num_pairs;
-  int32_t num_blocks;
+  int32_t src_blocks;      // blocks of the source / destination pools
+  int32_t dst_blocks;
   int64_t block_bytes;     // block_size * num_kv_heads * head_dim * element size (multiple of 64)
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
