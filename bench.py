@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--partition-size", type=int, default=1024)
+    p.add_argument("--layout", default="token",
+                   help="pool layout of the headline decode (token, head, unified_token, "
+                        "unified_head, layers_token, layers_head)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="wall-time budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -153,11 +156,24 @@ def timed(torch, stream, K, W, prefix, body, suffix=None):
     return start.elapsed_time(stop) / K, [a.elapsed_time(b) for a, b in ev]
 
 
-def secondary(torch, np, stream, K, W):
+def secondary(torch, np, stream, K, W, partition_size):
     from paged_kv_cache_87_amd import runner
     from paged_kv_cache_87_amd import workloads as wl
 
     out = {}
+    # the headline decode on each block layout of the pool, same timing
+    out["decode_layouts"] = {}
+    for layout in ("token", "head", "unified_head"):
+        w = wl.llama_gqa_decode(pool_fill="zero", partition_size=partition_size)
+        g = runner.GpuStep(w, layout=layout)
+        g.write_history()
+        _, dec_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend)
+        dec = float(np.mean(dec_ms))
+        out["decode_layouts"][layout] = {
+            "decode_us": dec * 1e3, "kv_GBps": w.kv_bytes_read() / (dec * 1e-3) / 1e9,
+            "frac_hbm_peak": w.kv_bytes_read() / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del g
+        torch.cuda.empty_cache()
     # batched causal prefill: slot mapping + write of every prompt token + prefill
     w = wl.batched_prefill(pool_fill="zero")
     g = runner.GpuStep(w)
@@ -280,7 +296,7 @@ def main():
 
     w = wl.llama_gqa_decode(pool_fill="zero", partition_size=args.partition_size,
                             fixed_context=args.fixed_context)
-    g = runner.GpuStep(w)
+    g = runner.GpuStep(w, layout=args.layout)
     g.write_history()
     kv_bytes = w.kv_bytes_read()
     stream = torch.cuda.current_stream()
@@ -294,10 +310,11 @@ def main():
     del g
     torch.cuda.empty_cache()
 
-    sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 30)
+    sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 30,
+                                                       args.partition_size)
     cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
 
-    traffic = measured_traffic(w.name, args.partition_size)
+    traffic = measured_traffic(w.name, args.partition_size) if args.layout == "token" else None
     rec = {
         "metric": METRIC,
         "value": kv_bytes / (step_ms * 1e-3) / 1e9,
@@ -325,6 +342,7 @@ def main():
             "sum_context_tokens": sum_ctx,
             "kv_bytes_per_step": kv_bytes,
             "partition_size": args.partition_size,
+            "pool_layout": args.layout,
         },
         "decode_us": {"mean": dec_avg_ms * 1e3, "p10": float(np.percentile(decode_ms, 10)) * 1e3,
                       "p50": float(np.percentile(decode_ms, 50)) * 1e3,

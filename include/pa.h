@@ -57,16 +57,42 @@ typedef enum pa_dtype {
   PA_BF16 = 1
 } pa_dtype;
 
+typedef enum pa_layout {
+  /* a block is [block_size, num_kv_heads, head_dim]: the Pico-vLLM pool tensor
+   * [2, num_layers, num_blocks, block_size, num_kv_heads, head_dim]
+   * ("核心数据结构和设计模式", BlockManager listing) */
+  PA_LAYOUT_TOKEN_MAJOR = 0,
+  /* a block is [num_kv_heads, block_size, head_dim]: JuliaPagedAttn's
+   * per-block K / V [head_dim, block_size, num_kv_heads] ("Block Layout"),
+   * which is column-major, read in row-major order; each KV head's 16 token
+   * rows of a block are one contiguous span */
+  PA_LAYOUT_HEAD_MAJOR = 1
+} pa_layout;
+
 /*
  * The block pool of one attention layer.
  *
- * k_cache and v_cache (device) are each a row-major, contiguous array
- * [num_blocks, block_size, num_kv_heads, head_dim] of `dtype` -- the
- * Pico-vLLM pool tensor [2, num_layers, num_blocks, block_size,
- * num_kv_heads, head_dim] ("核心数据结构和设计模式", BlockManager listing)
- * with its K/V and layer indices fixed; a multi-layer pool is passed one
- * layer at a time as two base pointers.  One block table addresses both
- * pools.  Both pointers must be 16-byte aligned.
+ * k_cache and v_cache (device) each hold num_blocks blocks of `dtype`; block
+ * b starts block_stride elements after block b - 1 and is laid out as
+ * `layout` says, densely (head_dim elements per token row of a head).
+ * block_stride == 0 means dense blocks (block_size * num_kv_heads *
+ * head_dim), i.e. a row-major [num_blocks, block_size, num_kv_heads,
+ * head_dim] (token-major) or [num_blocks, num_kv_heads, block_size,
+ * head_dim] (head-major) array.  One block table addresses both pools.
+ *
+ * The pages' pool variants map onto this descriptor as follows:
+ *   - one layer of a multi-layer pool [2, num_layers, num_blocks, ...]:
+ *     k_cache = &pool[0][layer], v_cache = &pool[1][layer], dense blocks;
+ *   - JuliaPagedAttn's 5-D K_cache / V_cache (column-major [head_dim,
+ *     block_size, num_kv_heads, num_blocks, num_layers]): k_cache =
+ *     &K_cache[layer], v_cache = &V_cache[layer], PA_LAYOUT_HEAD_MAJOR;
+ *   - K and V of a block stored together ([num_blocks, 2, block ...],
+ *     "unified K/V blocks" in JuliaPagedAttn "Features"): k_cache = &pool[0][0],
+ *     v_cache = &pool[0][1], block_stride = 2 * block elements.
+ *
+ * Both pointers must be 16-byte aligned; block_stride, if not 0, must be at
+ * least the dense block size and a multiple of 16 bytes.  Slots keep their
+ * meaning in every layout: slot = block * block_size + offset in the block.
  *
  * Supported: block_size 16, head_dim 64 or 128, dtype PA_F32 or PA_BF16.
  */
@@ -77,7 +103,9 @@ typedef struct pa_kv_pool {
   int32_t block_size;
   int32_t num_kv_heads;
   int32_t head_dim;
-  int32_t dtype; /* pa_dtype */
+  int32_t dtype;        /* pa_dtype */
+  int32_t layout;       /* pa_layout */
+  int64_t block_stride; /* elements from one block to the next; 0 = dense */
 } pa_kv_pool;
 
 /*
@@ -117,10 +145,12 @@ typedef struct pa_seq_desc {
  *     q_start_loc[s+1]-q_start_loc[s], and token q_start_loc[s]+i sits at
  *     position context_lens[s] - q_len + i (prefill, or a chunk of one).
  * slot_mapping (device, int64 [num_tokens], written):
- *   block_tables[s][pos / block_size] * block_size + pos % block_size, the
- *   flat row of the token in the pool viewed as [num_blocks * block_size,
- *   num_kv_heads, head_dim] (JuliaPagedAttn "Project Structure": slot mapping
- *   in the cache layout; nanoserve Day 19 "Diagram": slot_mapping).  -1 where
+ *   block_tables[s][pos / block_size] * block_size + pos % block_size: the
+ *   block and the offset of the token inside it (for a dense token-major
+ *   pool, the flat row of the token in the pool viewed as [num_blocks *
+ *   block_size, num_kv_heads, head_dim]; JuliaPagedAttn "Project Structure":
+ *   slot mapping in the cache layout; nanoserve Day 19 "Diagram":
+ *   slot_mapping).  -1 where
  *   the position is negative, at or past the context, past the table width,
  *   or the table entry is not a block of the pool.
  */

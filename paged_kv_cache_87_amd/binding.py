@@ -29,6 +29,9 @@ PA_F32 = 0
 PA_BF16 = 1
 PA_SWAP_OUT = 0
 PA_SWAP_IN = 1
+PA_LAYOUT_TOKEN_MAJOR = 0
+PA_LAYOUT_HEAD_MAJOR = 1
+LAYOUTS = {"token": PA_LAYOUT_TOKEN_MAJOR, "head": PA_LAYOUT_HEAD_MAJOR}
 
 EXPORTED = (
     "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill",
@@ -48,6 +51,8 @@ class PaKVPool(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("block_stride", ctypes.c_int64),
     ]
 
 
@@ -143,28 +148,72 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _pool_geometry(k: torch.Tensor, v: torch.Tensor, layout: str):
+    """(N, block_size, Hkv, D, block stride or 0) of K/V pools given as 4-D
+    tensors: ``[N, block_size, Hkv, D]`` (layout "token") or ``[N, Hkv,
+    block_size, D]`` (layout "head"), each block dense; the blocks may sit
+    further apart than their size (any stride of the first dimension, e.g.
+    ``pool[:, 0]`` / ``pool[:, 1]`` of a pool that keeps K and V of a block
+    together)."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    for n, t in (("k_cache", k), ("v_cache", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be 4-D (blocks, then the block's three dimensions)")
+        _, a, b, d = t.shape
+        if t.stride(3) != 1 or t.stride(2) != d or t.stride(1) != b * d:
+            raise ValueError(f"{n}: each block must be dense")
+    if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
+        raise ValueError("k_cache and v_cache must have the same shape, dtype and strides")
+    N, a, b, D = k.shape
+    B, H = (a, b) if layout == "token" else (b, a)
+    dense = a * b * D
+    stride = k.stride(0) if N > 1 else dense
+    if stride < dense:
+        raise ValueError("blocks overlap (first-dimension stride below the block size)")
+    return N, B, H, D, (0 if stride == dense else stride)
+
+
+def _pool_desc(k: torch.Tensor, v: torch.Tensor, layout: str, host: bool) -> PaKVPool:
+    N, B, H, D, stride = _pool_geometry(k, v, layout)
+    for n, t in (("k_cache", k), ("v_cache", v)):
+        if host:
+            if t.device.type != "cpu" or not t.is_pinned():
+                raise ValueError(f"{n} must be a pinned host tensor")
+        elif t.device.type != "cuda":
+            raise ValueError(f"{n} must be on the GPU")
+    return PaKVPool(k.data_ptr(), v.data_ptr(), N, B, H, D, _dtype_code(k.dtype), LAYOUTS[layout],
+                    stride)
+
+
 @dataclass
 class KVPool:
-    """K and V pools of one layer: ``[num_blocks, block_size, num_kv_heads,
-    head_dim]`` each, same dtype, on the GPU."""
+    """K and V pools of one layer on the GPU: ``[num_blocks, block_size,
+    num_kv_heads, head_dim]`` each (layout "token", the default) or
+    ``[num_blocks, num_kv_heads, block_size, head_dim]`` (layout "head"),
+    same dtype; views of a larger tensor (one layer of a multi-layer pool,
+    K and V halves of unified blocks) are fine as long as each block is
+    dense."""
 
     k_cache: torch.Tensor
     v_cache: torch.Tensor
+    layout: str = "token"
 
     def __post_init__(self):
-        if self.k_cache.shape != self.v_cache.shape or self.k_cache.dtype != self.v_cache.dtype:
-            raise ValueError("k_cache and v_cache must have the same shape and dtype")
-        if self.k_cache.dim() != 4:
-            raise ValueError("pools are [num_blocks, block_size, num_kv_heads, head_dim]")
+        _pool_geometry(self.k_cache, self.v_cache, self.layout)
 
     def c(self) -> PaKVPool:
-        N, B, H, D = self.k_cache.shape
-        return PaKVPool(_dev(self.k_cache, "k_cache"), _dev(self.v_cache, "v_cache"), N, B, H, D,
-                        _dtype_code(self.k_cache.dtype))
+        return _pool_desc(self.k_cache, self.v_cache, self.layout, host=False)
 
     @property
     def dtype(self):
         return self.k_cache.dtype
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
 
 
 @dataclass
@@ -202,7 +251,7 @@ def pa_slot_mapping(pool: KVPool, seqs: SeqDesc, slot_mapping: torch.Tensor,
 def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
                 slot_mapping: torch.Tensor, stream=None) -> None:
     lib = load_library()
-    _, _, H, D = pool.k_cache.shape
+    _, _, H, D, _ = _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)
     T = slot_mapping.numel()
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (T, H, D):
@@ -237,6 +286,8 @@ def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, s
     S, Hq, D = q.shape
     if tuple(out.shape) != (S, Hq, D):
         raise ValueError("out must have q's shape")
+    if D != _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)[3]:
+        raise ValueError("q's head_dim differs from the pool's")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")
@@ -254,6 +305,8 @@ def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
                stream=None) -> torch.Tensor:
     lib = load_library()
     T, Hq, D = q.shape
+    if D != _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)[3]:
+        raise ValueError("q's head_dim differs from the pool's")
     if tuple(out.shape) != (T, Hq, D):
         raise ValueError("out must have q's shape")
     cp, cs = pool.c(), seqs.c()
@@ -340,17 +393,10 @@ def pa_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=No
     _check("pa_copy_blocks", st)
 
 
-def host_pool_c(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaKVPool:
+def host_pool_c(k_cache: torch.Tensor, v_cache: torch.Tensor, layout: str = "token") -> PaKVPool:
     """Descriptor of a K/V pool held in pinned host memory (``pin_memory=True``
-    tensors, ``[num_blocks, block_size, num_kv_heads, head_dim]`` each)."""
-    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
-            raise ValueError(f"{n} must be a contiguous pinned host tensor")
-    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
-        raise ValueError("host k_cache and v_cache must be [N, block_size, Hkv, D] alike")
-    N, B, H, D = k_cache.shape
-    return PaKVPool(k_cache.data_ptr(), v_cache.data_ptr(), N, B, H, D,
-                    _dtype_code(k_cache.dtype))
+    tensors shaped as for ``KVPool``)."""
+    return _pool_desc(k_cache, v_cache, layout, host=True)
 
 
 def pa_swap_blocks(pool: KVPool, host_k: torch.Tensor, host_v: torch.Tensor,
@@ -358,7 +404,7 @@ def pa_swap_blocks(pool: KVPool, host_k: torch.Tensor, host_v: torch.Tensor,
                    stream=None) -> None:
     if device_blocks.shape != host_blocks.shape or device_blocks.dim() != 1:
         raise ValueError("device_blocks and host_blocks must be 1-D of the same length")
-    cp, ch = pool.c(), host_pool_c(host_k, host_v)
+    cp, ch = pool.c(), host_pool_c(host_k, host_v, pool.layout)
     st = load_library().pa_swap_blocks(
         ctypes.byref(cp), ctypes.byref(ch), _dev(device_blocks, "device_blocks", torch.int32),
         _dev(host_blocks, "host_blocks", torch.int32), int(device_blocks.shape[0]),
@@ -374,7 +420,8 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
     "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
-    "host_pool_c", "pa_swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN",
+    "host_pool_c", "pa_swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
+    "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",
     "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
     "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_BLOCKS", "PA_F32", "PA_BF16",
 ]

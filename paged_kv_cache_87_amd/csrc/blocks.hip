@@ -5,8 +5,10 @@
 // block of the K pool and the same block of the V pool, bit for bit.
 //
 // grid (pair, pool, quarter of the block), 256 threads; each thread moves
-// 16-byte chunks with a stride of one workgroup.  Pairs whose ids are outside
-// the pool are skipped.
+// 16-byte chunks with a stride of one workgroup.  A block's rows fill one
+// contiguous span in every supported layout, so a block is copied as bytes;
+// blocks may sit further apart than their span (K and V of a block stored
+// together).  Pairs whose ids are outside the pool are skipped.
 //
 // The same kernel moves blocks between the device pool and a pool in pinned
 // host memory (Pico-vLLM #5 Paged Attention, BlockManager swap_out /
@@ -33,8 +35,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
   const int64_t chunks = a.block_bytes >> 4;          // 16-byte chunks per block
   const int64_t per = chunks / kCopySplit;
   const int64_t c0 = per * blockIdx.z;
-  const uint4* s = reinterpret_cast<const uint4*>(base + static_cast<int64_t>(src) * a.block_bytes);
-  uint4* d = reinterpret_cast<uint4*>(out + static_cast<int64_t>(dst) * a.block_bytes);
+  const uint4* s = reinterpret_cast<const uint4*>(base + static_cast<int64_t>(src) * a.src_stride);
+  uint4* d = reinterpret_cast<uint4*>(out + static_cast<int64_t>(dst) * a.dst_stride);
   for (int64_t c = c0 + threadIdx.x; c < c0 + per; c += kCopyThreads) d[c] = s[c];
 }
 

@@ -427,8 +427,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int slot_head[N];                  // head carried by accumulator slot j
   bcast_all_i<R>(own, slot_head);
 
-  const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * LT::kElt;
-  const uint32_t block_bytes = row_bytes * kBlockSize;
+  // token rows of one KV head: token_stride apart, head_stride between heads
+  // (token-major or head-major blocks); a block's rows fill `span` bytes
+  const uint32_t row_bytes = a.geom.token_stride;
+  const uint32_t head_bytes = a.geom.head_stride;
+  const uint32_t block_bytes = a.geom.span;
+  const int64_t block_stride = a.geom.block_stride;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   const float sl2 = a.scale_log2;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int tbl = load_tbl(cur, c0);
   uint32_t qv[N][NW];
   load_q(cur, qv);
-  uint32_t lane_off = (cur.g * D + li * EPL) * LT::kElt + row * row_bytes;
+  uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
   auto chunk_blocks = [&](const Seg& x, int cs) {
     const int ce = min(x.blk1, cs + kChunkBlocks);
     return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     const bool ok = phys >= 0 && phys < a.num_blocks;
     if (!ok) nvalid = 0;
-    const int64_t off = ok ? static_cast<int64_t>(phys) * block_bytes : 0;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride : 0;
     const Rsrc rk = make_rsrc(kpool + off, ok ? block_bytes : 0u);
     const Rsrc rv = make_rsrc(vpool + off, ok ? block_bytes : 0u);
 #pragma unroll
@@ -719,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
     c0 = cur.blk0;
     nk = chunk_blocks(cur, c0);
-    lane_off = (cur.g * D + li * EPL) * LT::kElt + row * row_bytes;
+    lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
     m = kNegBig;
     l = 0.f;
 #pragma unroll

@@ -55,7 +55,47 @@ pa_status check_pool(const pa_kv_pool* pool) {
     return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", pool->block_size);
   if (pool->head_dim != 64 && pool->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", pool->head_dim);
+  if (pool->num_kv_heads > 4096)
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d (at most 4096)", pool->num_kv_heads);
+  if (pool->layout != PA_LAYOUT_TOKEN_MAJOR && pool->layout != PA_LAYOUT_HEAD_MAJOR)
+    return fail(PA_ERR_INVALID_ARG, "unknown layout %d", pool->layout);
+  const int64_t dense = static_cast<int64_t>(pool->block_size) * pool->num_kv_heads *
+                        pool->head_dim;
+  if (pool->block_stride != 0) {
+    if (pool->block_stride < dense)
+      return fail(PA_ERR_INVALID_ARG, "block_stride %lld is below the block's %lld elements",
+                  static_cast<long long>(pool->block_stride), static_cast<long long>(dense));
+    if ((pool->block_stride * elt_size(pool->dtype)) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "block_stride %lld is not a multiple of 16 bytes",
+                  static_cast<long long>(pool->block_stride));
+    if (pool->block_stride > (int64_t(1) << 40) / pool->num_blocks)
+      return fail(PA_ERR_UNSUPPORTED, "block_stride %lld x num_blocks %d is too large",
+                  static_cast<long long>(pool->block_stride), pool->num_blocks);
+  }
   return PA_OK;
+}
+
+// Byte geometry of a checked pool.
+pa::PoolGeom geom_of(const pa_kv_pool* p) {
+  const int e = elt_size(p->dtype);
+  const uint32_t row = static_cast<uint32_t>(p->head_dim * e);
+  pa::PoolGeom g{};
+  g.span = static_cast<uint32_t>(p->block_size) * p->num_kv_heads * row;
+  g.block_stride = p->block_stride != 0 ? p->block_stride * e : static_cast<int64_t>(g.span);
+  if (p->layout == PA_LAYOUT_TOKEN_MAJOR) {
+    g.token_stride = static_cast<uint32_t>(p->num_kv_heads) * row;
+    g.head_stride = row;
+  } else {
+    g.token_stride = row;
+    g.head_stride = static_cast<uint32_t>(p->block_size) * row;
+  }
+  return g;
+}
+
+// Bytes from a pool's base pointer to the end of its last block.
+size_t extent_bytes(const pa_kv_pool* p) {
+  const pa::PoolGeom g = geom_of(p);
+  return static_cast<size_t>(g.block_stride) * (p->num_blocks - 1) + g.span;
 }
 
 pa_status check_seqs(const pa_seq_desc* seqs) {
@@ -192,7 +232,7 @@ const char* pa_status_string(int32_t status) {
 
 const char* pa_last_error(void) { return g_last_error; }
 
-int32_t pa_version(void) { return (1 << 16) | 0; }
+int32_t pa_version(void) { return (1 << 16) | 1; }
 
 pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
                           const int32_t* q_start_loc, int32_t num_tokens,
@@ -226,7 +266,8 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
     return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   pa::WriteKVArgs a{k_new, v_new, pool->k_cache, pool->v_cache, slot_mapping, num_tokens,
                     pool->num_kv_heads * pool->head_dim * elt_size(pool->dtype),
-                    static_cast<int64_t>(pool->num_blocks) * pool->block_size};
+                    pool->head_dim * elt_size(pool->dtype),
+                    static_cast<int64_t>(pool->num_blocks) * pool->block_size, geom_of(pool)};
   return hip_status(pa::launch_write_kv(a, stream), "write_kv launch");
 }
 
@@ -241,10 +282,10 @@ pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
     return fail(PA_ERR_INVALID_ARG, "src_blocks or dst_blocks is null");
   if (num_pairs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "num_pairs %d (at most 65535 a call)", num_pairs);
+  const pa::PoolGeom g = geom_of(pool);
   pa::CopyBlocksArgs a{pool->k_cache, pool->v_cache, pool->k_cache, pool->v_cache,
                        src_blocks, dst_blocks, num_pairs, pool->num_blocks, pool->num_blocks,
-                       static_cast<int64_t>(pool->block_size) * pool->num_kv_heads *
-                           pool->head_dim * elt_size(pool->dtype)};
+                       g.span, g.block_stride, g.block_stride};
   return hip_status(pa::launch_copy_blocks(a, stream), "copy_blocks launch");
 }
 
@@ -257,8 +298,10 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
   if ((st = check_pool(host_pool)) != PA_OK) return st;
   if (host_pool->block_size != device_pool->block_size ||
       host_pool->num_kv_heads != device_pool->num_kv_heads ||
-      host_pool->head_dim != device_pool->head_dim || host_pool->dtype != device_pool->dtype)
-    return fail(PA_ERR_INVALID_ARG, "host and device pools differ in block shape or dtype");
+      host_pool->head_dim != device_pool->head_dim || host_pool->dtype != device_pool->dtype ||
+      host_pool->layout != device_pool->layout)
+    return fail(PA_ERR_INVALID_ARG,
+                "host and device pools differ in block shape, dtype or layout");
   if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
     return fail(PA_ERR_INVALID_ARG, "direction %d", direction);
   if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs %d", num_pairs);
@@ -267,14 +310,12 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
     return fail(PA_ERR_INVALID_ARG, "device_blocks or host_blocks is null");
   if (num_pairs > 65535)
     return fail(PA_ERR_UNSUPPORTED, "num_pairs %d (at most 65535 a call)", num_pairs);
-  const int64_t bb = static_cast<int64_t>(device_pool->block_size) * device_pool->num_kv_heads *
-                     device_pool->head_dim * elt_size(device_pool->dtype);
   const size_t ids = sizeof(int32_t) * static_cast<size_t>(num_pairs);
   for (const void* p : {device_pool->k_cache, device_pool->v_cache})
-    if (!device_addressable(p, bb * device_pool->num_blocks, false))
+    if (!device_addressable(p, extent_bytes(device_pool), false))
       return fail(PA_ERR_INVALID_ARG, "device pool is not device memory of the current device");
   for (const void* p : {host_pool->k_cache, host_pool->v_cache})
-    if (!device_addressable(p, bb * host_pool->num_blocks, true))
+    if (!device_addressable(p, extent_bytes(host_pool), true))
       return fail(PA_ERR_INVALID_ARG,
                   "host pool is not pinned host memory mapped at the same address");
   for (const void* p : {static_cast<const void*>(device_blocks),
@@ -284,9 +325,11 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
   const bool out = direction == PA_SWAP_OUT;
   const pa_kv_pool* s = out ? device_pool : host_pool;
   const pa_kv_pool* d = out ? host_pool : device_pool;
+  const pa::PoolGeom gs = geom_of(s), gd = geom_of(d);
   pa::CopyBlocksArgs a{s->k_cache, s->v_cache, d->k_cache, d->v_cache,
                        out ? device_blocks : host_blocks, out ? host_blocks : device_blocks,
-                       num_pairs, s->num_blocks, d->num_blocks, bb};
+                       num_pairs, s->num_blocks, d->num_blocks, gs.span, gs.block_stride,
+                       gd.block_stride};
   return hip_status(pa::launch_copy_blocks(a, stream), "swap_blocks launch");
 }
 
@@ -366,6 +409,7 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   a.min_slice_blocks = plan.min_slice_blocks;
   a.max_slices = plan.max_slices;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.geom = geom_of(pool);
   return hip_status(pa::launch_decode(a, stream), "decode launch");
 }
 
@@ -406,6 +450,7 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
   a.max_q_len = max_q_len;
   a.total_q_tokens = total_q_tokens;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.geom = geom_of(pool);
   return hip_status(pa::launch_prefill(a, stream), "prefill launch");
 }
 

@@ -17,6 +17,16 @@ pa_status report(pa_status status, const char* fmt, ...);
 
 constexpr int kBlockSize = 16;  // tokens per physical block the kernels handle
 
+// Where a (block, token, KV head) row of head_dim elements sits in a pool, in
+// bytes: block * block_stride + token * token_stride + head * head_stride.
+// A block's rows fill one span of `span` bytes in every supported layout.
+struct PoolGeom {
+  int64_t block_stride;
+  uint32_t token_stride;   // token-major: num_kv_heads * head row; head-major: one head row
+  uint32_t head_stride;    // token-major: one head row; head-major: block_size head rows
+  uint32_t span;           // block_size * num_kv_heads * head_dim * element size
+};
+
 struct SlotMappingArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
@@ -37,7 +47,9 @@ struct WriteKVArgs {
   const int64_t* slot_mapping;
   int32_t num_tokens;
   int32_t row_bytes;       // num_kv_heads * head_dim * element size (multiple of 16)
+  int32_t head_bytes;      // head_dim * element size (multiple of 16)
   int64_t num_slots;       // num_blocks * block_size
+  PoolGeom geom;
 };
 hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream);
 
@@ -51,7 +63,10 @@ struct CopyBlocksArgs {
   int32_t num_pairs;
   int32_t src_blocks;      // blocks of the source / destination pools
   int32_t dst_blocks;
-  int64_t block_bytes;     // block_size * num_kv_heads * head_dim * element size (multiple of 64)
+  int64_t block_bytes;     // block span, block_size * num_kv_heads * head_dim * element size
+                           // (multiple of 64)
+  int64_t src_stride;      // bytes from one block to the next in the source / destination
+  int64_t dst_stride;
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
@@ -76,6 +91,7 @@ struct DecodeArgs {
   int32_t min_slice_blocks;  // 0: every (sequence, KV head) in one pass; else split
   int32_t max_slices;      // split: upper bound of the grid (partial slots = 2x)
   float scale_log2;        // softmax scale * log2(e)
+  PoolGeom geom;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -97,6 +113,7 @@ struct PrefillArgs {
   int32_t max_q_len;
   int32_t total_q_tokens;
   float scale_log2;
+  PoolGeom geom;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

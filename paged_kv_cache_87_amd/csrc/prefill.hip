@@ -128,8 +128,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int key_end = first_pos + last_tok + 1;       // keys [0, key_end)
   const int n_kt = (key_end + kKeys - 1) / kKeys;
   const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * kD * 2;
-  const uint32_t block_bytes = row_bytes * kBlockSize;
+  const uint32_t row_bytes = a.geom.token_stride;     // next token row of one KV head
+  const uint32_t block_bytes = a.geom.span;           // a block's rows (both layouts)
 
   // ---- K/V tile loader: 64 keys x 128 d, K and V as [key][d] rows -----------
   // thread -> (key pair 8 w + 2 (lane / 16) (+32 for the second pass), d chunk
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // descriptor's size), so no pool row outside the context reaches the P.V
   const int ld_key = 8 * wave + 2 * (lane >> 4);   // 0, 2, ..., 30
   const int ld_dc = lane & 15;                      // 8-element chunk of d
-  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + (g * kD + ld_dc * 8) * 2;
+  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   auto load_ids = [&](int kt, int (&ids)[2]) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     for (int ps = 0; ps < 2; ++ps) {
       const int phys = uniform(ids[ps]);
       const bool ok = phys >= 0 && phys < a.num_blocks;
-      const int64_t boff = ok ? static_cast<int64_t>(phys) * block_bytes : 0;
+      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
       const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
       const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
 #pragma unroll

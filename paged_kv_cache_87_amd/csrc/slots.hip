@@ -7,7 +7,9 @@
 // (JuliaPagedAttn README, "Project Structure": slot mapping in the cache
 // layout; nanoserve Day 19, "Diagram": slot_mapping).  The write copies each
 // new token's [Hkv, D] row into its slot bit for bit (JuliaPagedAttn "API
-// Reference": write_kv_cache!; nanoserve Day 19 "What I added today").
+// Reference": write_kv_cache!; nanoserve Day 19 "What I added today"), in
+// whichever block layout the pool has (token-major as the Pico-vLLM pool, or
+// head-major as JuliaPagedAttn's "Block Layout").
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -53,9 +55,13 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingA
   a.slot_mapping[i] = slot;
 }
 
-// One 16-byte chunk per thread; blockIdx.y selects K (0) or V (1).
+// One 16-byte chunk per thread; blockIdx.y selects K (0) or V (1).  The
+// source row of a token is [Hkv, D]; chunk `part` of it belongs to KV head
+// part / (chunks per head row) and lands where the pool's layout puts that
+// head's row of the slot's block.
 __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) {
   const int chunks_per_row = a.row_bytes >> 4;
+  const int chunks_per_head = a.head_bytes >> 4;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x;
   const int64_t total = static_cast<int64_t>(a.num_tokens) * chunks_per_row;
   if (c >= total) return;
@@ -63,9 +69,16 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) 
   const int part = static_cast<int>(c - static_cast<int64_t>(t) * chunks_per_row);
   const int64_t slot = a.slot_mapping[t];
   if (slot < 0 || slot >= a.num_slots) return;
+  const int h = part / chunks_per_head;
+  const int q = part - h * chunks_per_head;
+  const int64_t blk = slot / kBlockSize;
+  const int in_blk = static_cast<int>(slot - blk * kBlockSize);
+  const int64_t dst_off = blk * a.geom.block_stride +
+                          static_cast<int64_t>(in_blk) * a.geom.token_stride +
+                          static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;
   const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
-  uint4* dst = static_cast<uint4*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
-  dst[slot * chunks_per_row + part] = src[static_cast<int64_t>(t) * chunks_per_row + part];
+  char* dst = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  *reinterpret_cast<uint4*>(dst + dst_off) = src[static_cast<int64_t>(t) * chunks_per_row + part];
 }
 
 }  // namespace

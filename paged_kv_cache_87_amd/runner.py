@@ -37,25 +37,32 @@ def i32(a, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
 
 
+# Pool layouts a step can run on: the block layout and how the K and V pools
+# are held (separate arrays; K and V of a block side by side; one layer of a
+# [2, layers, N, block] pool; one layer of per-layer K and V arrays).
+POOL_LAYOUTS = {
+    "token": ("token", "separate"),
+    "head": ("head", "separate"),
+    "unified_token": ("token", "unified"),
+    "unified_head": ("head", "unified"),
+    "layers_token": ("token", "layers"),
+    "layers_head": ("head", "per_layer"),
+}
+POOL_LAYERS, POOL_LAYER = 3, 1
+
+
 class GpuStep:
     """Device-resident copy of a workload, ready to run its step."""
 
-    def __init__(self, w: Workload, device="cuda", partition_size=None):
+    def __init__(self, w: Workload, device="cuda", partition_size=None, layout="token"):
         self.w = w
         self.device = device
         self.partition_size = w.partition_size if partition_size is None else partition_size
+        self.layout = layout
         tdt = torch.float32 if w.dtype == F32 else torch.bfloat16
-        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-        if w.pool_fill == "nan":
-            if w.dtype == F32:
-                self.k_cache = torch.full(shape, float("nan"), dtype=tdt, device=device)
-            else:
-                self.k_cache = torch.full(shape, BF16_NAN_BITS, dtype=torch.int16,
-                                          device=device).view(torch.bfloat16)
-        else:
-            self.k_cache = torch.zeros(shape, dtype=tdt, device=device)
-        self.v_cache = self.k_cache.clone()
-        self.pool = pa.KVPool(self.k_cache, self.v_cache)
+        self.storage = [self._filled(shape, tdt) for shape in self._storage_shapes(layout)]
+        self.k_cache, self.v_cache = self._views(layout, self.storage)
+        self.pool = pa.KVPool(self.k_cache, self.v_cache, POOL_LAYOUTS[layout][0])
         self.block_tables = i32(w.block_tables, device)
         self.context_lens = i32(w.context_lens, device)
         self.seqs = pa.SeqDesc(self.block_tables, self.context_lens, w.max_context_len)
@@ -71,6 +78,39 @@ class GpuStep:
         self.workspace = pa.decode_workspace(self.pool, self.seqs, w.num_q_heads,
                                              self.partition_size,
                                              device) if w.kind == "decode" else None
+
+    def _filled(self, shape, tdt):
+        w = self.w
+        if w.pool_fill != "nan":
+            return torch.zeros(shape, dtype=tdt, device=self.device)
+        if w.dtype == F32:
+            return torch.full(shape, float("nan"), dtype=tdt, device=self.device)
+        return torch.full(shape, BF16_NAN_BITS, dtype=torch.int16,
+                          device=self.device).view(torch.bfloat16)
+
+    def _storage_shapes(self, layout):
+        w = self.w
+        N, B, H, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim
+        blk = (B, H, D) if POOL_LAYOUTS[layout][0] == "token" else (H, B, D)
+        kind = POOL_LAYOUTS[layout][1]
+        if kind == "separate":          # one [N, block] array each for K and V
+            return [(N, *blk), (N, *blk)]
+        if kind == "unified":           # K and V of a block side by side
+            return [(N, 2, *blk)]
+        if kind == "layers":            # [2, layers, N, block], one layer used
+            return [(2, POOL_LAYERS, N, *blk)]
+        return [(POOL_LAYERS, N, *blk), (POOL_LAYERS, N, *blk)]   # per-layer K and V arrays
+
+    @staticmethod
+    def _views(layout, st):
+        kind = POOL_LAYOUTS[layout][1]
+        if kind == "separate":
+            return st[0], st[1]
+        if kind == "unified":
+            return st[0][:, 0], st[0][:, 1]
+        if kind == "layers":
+            return st[0][0, POOL_LAYER], st[0][1, POOL_LAYER]
+        return st[0][POOL_LAYER], st[1][POOL_LAYER]
 
     # -- setup: history written before the step ------------------------------
     def write_history(self):
@@ -122,15 +162,20 @@ class GpuStep:
         return self.out.float().cpu().numpy().astype(np.float64)
 
     def pools_stored(self):
-        return to_host_stored(self.k_cache), to_host_stored(self.v_cache)
+        """K and V pools as stored values, [num_blocks, block_size, Hkv, D]
+        whatever the layout."""
+        k, v = to_host_stored(self.k_cache), to_host_stored(self.v_cache)
+        if POOL_LAYOUTS[self.layout][0] == "head":
+            k, v = k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3)
+        return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
 
-def run_workload(w: Workload, partition_size=None) -> GpuStep:
-    g = GpuStep(w, partition_size=partition_size)
+def run_workload(w: Workload, partition_size=None, layout="token") -> GpuStep:
+    g = GpuStep(w, partition_size=partition_size, layout=layout)
     g.write_history()
     g.step()
     torch.cuda.synchronize()
     return g
 
 
-__all__ = ["GpuStep", "run_workload", "to_device", "to_host_stored", "i32", "BF16", "F32"]
+__all__ = ["GpuStep", "run_workload", "POOL_LAYOUTS", "to_device", "to_host_stored", "i32", "BF16", "F32"]
