@@ -67,10 +67,12 @@ class GpuStep:
         self.context_lens = i32(w.context_lens, device)
         self.seqs = pa.SeqDesc(self.block_tables, self.context_lens, w.max_context_len)
         self.q = to_device(w.q, w.dtype, device)
-        self.out = torch.empty_like(self.q)
+        # NaN until a kernel writes it, so a row the kernels skip cannot pass
+        # for a result left in reused memory
+        self.out = torch.full_like(self.q, float("nan"))
         self.new_k = to_device(w.new_k, w.dtype, device)
         self.new_v = to_device(w.new_v, w.dtype, device)
-        self.slots = torch.empty(w.new_k.shape[0], dtype=torch.int64, device=device)
+        self.slots = torch.full((w.new_k.shape[0],), -7, dtype=torch.int64, device=device)
         self.q_start_loc = None if w.q_start_loc is None else i32(w.q_start_loc, device)
         self.max_q_len = 0
         if w.q_start_loc is not None:

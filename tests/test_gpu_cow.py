@@ -111,11 +111,11 @@ def test_copy_on_write_decode_step():
                    torch.from_numpy(prefix_slots).cuda())
     pa.pa_copy_blocks(pool, runner.i32([c[0] for c in copies]), runner.i32([c[1] for c in copies]))
     seqs = pa.SeqDesc(runner.i32(tab), runner.i32(lens), P + 1)
-    slots = torch.empty(S, dtype=torch.int64, device="cuda")
+    slots = torch.full((S,), -7, dtype=torch.int64, device="cuda")
     pa.pa_slot_mapping(pool, seqs, slots)
     pa.pa_write_kv(pool, runner.to_device(nk, dtype), runner.to_device(nv, dtype), slots)
     qg = runner.to_device(q, dtype)
-    out = torch.empty_like(qg)
+    out = torch.full_like(qg, float("nan"))   # a skipped row stays NaN
     pa.pa_decode(pool, seqs, qg, out, scale, 0, None)
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), slots_ref)

@@ -90,7 +90,7 @@ def test_prefill_row_equals_decode():
     tables = g.block_tables.expand(len(rows), -1).contiguous()
     seqs = pa.SeqDesc(tables, lens, 300)
     q = g.q[rows].contiguous()
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))   # a skipped row stays NaN
     pa.pa_decode(g.pool, seqs, q, out, w.scale, 0, None)
     torch.cuda.synchronize()
     a = g.out[rows].float().cpu().numpy().astype(np.float64)
@@ -150,7 +150,7 @@ def test_mixed_decode_and_prefill_batch():
     seqs = pa.SeqDesc(g.block_tables.index_select(0, idx).contiguous(),
                       g.context_lens.index_select(0, idx).contiguous(), max(lens))
     q = g.q[rows].contiguous()
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))   # a skipped row stays NaN
     for part in (0, 512):
         ws = pa.decode_workspace(g.pool, seqs, w.num_q_heads, part) if part else None
         pa.pa_decode(g.pool, seqs, q, out, w.scale, part, ws)
