@@ -6,10 +6,11 @@
 // the whole history through the block table in place).
 //
 // Work decomposition
-//   A persistent grid of 256-thread workgroups (4 waves) walks segments of
-//   (sequence, KV head) pairs: whole pairs, or equal slices of the batch's
-//   blocks when the context is split (see the driver below); the waves of a
-//   workgroup take a segment's blocks round-robin.
+//   A persistent grid of workgroups (eight waves, one workgroup per CU; four
+//   for the register-heavy variants) walks segments of (sequence, KV head)
+//   pairs: whole pairs, or equal slices of the batch's work when the context
+//   is split (see the driver below); the waves of a workgroup take a
+//   segment's blocks round-robin.
 //   Inside a wave the 64 lanes form four 16-lane DPP rows.  Row r handles
 //   tokens r, r+4, r+8, r+12 of the wave's current 16-token block; lane i of
 //   the row owns elements [i*D/16, (i+1)*D/16) of the head dimension, so one
@@ -47,10 +48,19 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup.  One workgroup of eight waves per CU streams a
+// segment's blocks with all of them: the waves of one CU then share each
+// segment instead of two workgroups of four competing for it (the older of
+// two co-resident workgroups wins the issue arbitration and the younger one
+// trails it by about a quarter).  Variants whose registers do not fit two
+// waves per SIMD (wide fp32 rows with many query heads) keep four.
+template <typename T, int D, int R>
+constexpr int decode_waves() {
+  constexpr int NW = D * static_cast<int>(sizeof(T)) / 64;       // dwords per lane per token row
+  constexpr int footprint = 16 * NW + (1 << R) * (D / 16 + NW);  // ring + accumulators + query
+  return footprint >= 160 ? 4 : 8;
+}
 constexpr float kNegBig = -1.0e30f;  // "no score yet": finite, so m - m stays 0
-constexpr int kChunkBlocks = 64 * kWaves;  // blocks whose table entries one load brings in
 constexpr int kRing = 2;                    // blocks per wave in the load ring
 constexpr float kRescaleLog2 = 8.f;         // reference-max slack before a rescale
 constexpr int kKVPolicy = 2;                // K/V loads are non-temporal: each byte is read once
@@ -177,21 +187,23 @@ __device__ __forceinline__ float load_shared(const float* p) {
 // N query heads of its group: out = sum_j w_j o_j / sum_j w_j with
 // w_j = l_j * 2^(m_j - max m), o_j a piece's normalised output (JuliaPagedAttn
 // "Online Softmax": the same max/sum rescaling that joins two blocks joins
-// two pieces), taken in token order with a running maximum.  The pair covers
-// flat blocks [A, E); its piece in slice i sits in partial slot 2i, or 2i + 1
-// for the first slice when the pair starts inside it.  Each thread owns E_
+// two pieces), taken in token order with a running maximum.  The pair's
+// blocks sit at work positions [A, E) and its work range starts at A0 <= A;
+// its piece in slice i sits in partial slot 2i, or 2i + 1 for the first
+// slice when that slice starts before the pair's work range (then an
+// earlier pair's segment came first in it).  Each thread owns E_
 // output elements; the loads of eight pieces are issued together, so a merge
 // of up to eight pieces costs one memory round trip.
 constexpr int kMergeBatch = 8;
 
-template <typename T, int D, int N>
-__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, int A, int E,
-                                           int Q, int tid) {
+template <typename T, int D, int N, int kThreads>
+__device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, int A0, int A,
+                                           int E, int Q, int tid) {
   constexpr int kOut = N * D;
   constexpr int E_ = (kOut + kThreads - 1) / kThreads;
   const int ia = A / Q;
   const int n = (E - 1) / Q - ia + 1;
-  const bool first_tail = A != ia * Q;
+  const bool first_tail = ia * Q < A0;
   float M[E_], wsum[E_], osum[E_];
   int hd[E_], dd[E_];
 #pragma unroll
@@ -243,16 +255,20 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 }
 
 // Persistent driver.  Each workgroup first builds, in LDS, the plan of the
-// whole batch: clamped context lengths and the prefix sum of blocks per KV
+// whole batch: clamped context lengths and the prefix sum of the work per KV
 // head.  Pair p = s * Hkv + g (sequence s, KV head g) owns nb_s =
-// ceil(L_s / 16) blocks, laid end to end at flat offset
-// A_p = Hkv * pre_s + g * nb_s, B blocks in all.
+// ceil(L_s / 16) blocks.  Its work is priced at c_s = nb_s + seg_cost
+// block-equivalents (0 for an empty context): the blocks, plus the fixed
+// cost of a segment (its epilogue and the restart of its load ring), so
+// that a slice full of short pairs is not overloaded.  The pairs' work
+// ranges lie end to end at W_p = Hkv * pre_s + g * c_s, B in all; block j
+// of the pair sits at W_p + seg_cost + j.
 //
-// Split (min_slice_blocks > 0): the flat range is cut into slices of
-// Q = max(ceil(B / grid), min_slice_blocks) blocks and workgroup i takes
-// slice i, so every workgroup streams the same number of bytes whatever the
-// mix of context lengths.  The part of a pair inside a slice (a segment)
-// keeps its own online-softmax state.  Only the first and the last segment
+// Split (min_slice_blocks > 0): the work range is cut into slices of
+// Q = max(ceil(B / grid), min_slice_blocks) and workgroup i takes slice i,
+// so every workgroup gets the same work whatever the mix of context
+// lengths.  The part of a pair inside a slice (a segment: the pair's blocks
+// whose positions fall in the slice) keeps its own online-softmax state.  Only the first and the last segment
 // of a slice can be pieces of a pair that goes on in another slice; they
 // write (o, m, l) to partial slots 2i and 2i + 1, the segments between them
 // are whole pairs and write `out`.  At the end of its slice a workgroup
@@ -260,7 +276,7 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 // of a pair merges it.  Without a split, workgroup i takes pairs i,
 // i + grid, ... whole.
 //
-// Inside a segment the four waves take its blocks round-robin, each through
+// Inside a segment the waves take its blocks round-robin, each through
 // a ring of kRing register buffers (kRing-1 blocks in flight while one is
 // computed).  Between segments nothing drains: while one computes, the table
 // entries of the next are already loaded, and the query rows and first ring
@@ -272,7 +288,10 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 // Plan in dynamic LDS: ctx[S] clamped context lengths, pre[S+1] exclusive
 // prefix sum of blocks per KV head.
 template <typename T, int D, int R>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(DecodeArgs a) {
+  constexpr int kWaves = decode_waves<T, D, R>();
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kChunkBlocks = 64 * kWaves;  // blocks whose table entries one load brings in
   using LT = Layout<T, D>;
   constexpr int N = 1 << R;          // query heads per KV head
   constexpr int W = 16 >> R;         // lanes per head after the reduce-scatter
@@ -307,16 +326,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       int L = a.context_lens[q];
       L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
       sm_ctx[q] = L;
-      cb += (L + kBlockSize - 1) / kBlockSize;
+      cb += L > 0 ? (L + kBlockSize - 1) / kBlockSize + a.seg_cost : 0;
     }
     sm_scan[tid] = cb;
     __syncthreads();
     if (tid < 64) {
-      // exclusive scan of the 256 per-thread counts: 4 per lane, then the wave
-      int c[4], t = 0;
+      // exclusive scan of the per-thread counts: kThreads / 64 per lane, then the wave
+      int c[kThreads / 64], t = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = sm_scan[4 * tid + i];
+      for (int i = 0; i < kThreads / 64; ++i) {
+        c[i] = sm_scan[kThreads / 64 * tid + i];
         t += c[i];
       }
       int x = t;
@@ -327,8 +346,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
       int e = x - t;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm_scan[4 * tid + i] = e;
+      for (int i = 0; i < kThreads / 64; ++i) {
+        sm_scan[kThreads / 64 * tid + i] = e;
         e += c[i];
       }
       if (tid == 63) sm_pre[S] = x;
@@ -337,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     int e = sm_scan[tid];
     for (int q = b0; q < b1; ++q) {
       sm_pre[q] = e;
-      e += (sm_ctx[q] + kBlockSize - 1) / kBlockSize;
+      e += sm_ctx[q] > 0 ? (sm_ctx[q] + kBlockSize - 1) / kBlockSize + a.seg_cost : 0;
     }
     __syncthreads();
   }
@@ -361,17 +380,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     F0 = static_cast<int>(f0 < B ? f0 : B);
     F1 = static_cast<int>(f0 + Q < B ? f0 + Q : B);
   }
-  auto nb_of = [&](int q) { return sm_pre[q + 1] - sm_pre[q]; };
+  const int C = a.seg_cost;
+  auto nb_of = [&](int q) { return (sm_ctx[q] + kBlockSize - 1) / kBlockSize; };
+  auto cost_of = [&](int q) { return sm_pre[q + 1] - sm_pre[q]; };
   struct Seg {
     int s, g, L, tok1, blk0, blk1;
     int slot;                        // partial slot, or -1: a whole pair, written to out
+    int end;                         // split: work position just past the segment
   };
   // segment starting at `pos`: a flat block (split) or a pair index
+  // segment of the pair whose work range holds `pos` (split: a work
+  // position; may be empty when the slice ends before the pair's first block)
   auto seg_at = [&](int pos) {
     Seg x;
     if (split) {
-      // last sequence whose blocks start at or before pos (a run of empty
-      // sequences ends at the one that owns the block)
+      // last sequence whose work starts at or before pos (a run of empty
+      // sequences ends at the one that owns the position)
       int lo = 0, hi = S - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -379,10 +403,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
       x.s = lo;
       const int nb = nb_of(lo);
+      const int cw = cost_of(lo);
       const int off = pos - Hkv * sm_pre[lo];
-      x.g = off / nb;
-      x.blk0 = off - x.g * nb;
-      x.blk1 = min(nb, x.blk0 + (F1 - pos));
+      x.g = off / cw;
+      const int first_blk = Hkv * sm_pre[lo] + x.g * cw + C;   // work position of block 0
+      x.blk0 = max(0, pos - first_blk);
+      x.blk1 = min(nb, F1 - first_blk);
+      x.end = first_blk + x.blk1;
       x.slot = (x.blk0 == 0 && x.blk1 == nb) ? -1
              : 2 * static_cast<int>(blockIdx.x) + (pos == F0 ? 0 : 1);
     } else {
@@ -401,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     return p;
   };
   auto next_pos = [&](const Seg& x, int pos) {
-    return split ? pos + (x.blk1 - x.blk0) : skip_empty(pos + gridDim.x);
+    return split ? x.end : skip_empty(pos + gridDim.x);
   };
   const int pos_end = split ? F1 : n_pairs;
   // lane t: table entry of this wave's t-th block of the chunk at c0
@@ -441,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int pos = split ? F0 : skip_empty(blockIdx.x);
   if (pos >= pos_end) return;
   Seg cur = seg_at(pos);
+  if (cur.blk1 <= cur.blk0) return;  // the slice holds no block
   int c0 = cur.blk0;                 // first block of the current chunk
   int nk = 0;                        // this wave's blocks in the current chunk
   int tbl = load_tbl(cur, c0);
@@ -589,6 +617,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   int pos_n = next_pos(cur, pos);
   bool has_next = pos_n < pos_end;
   Seg nxt = has_next ? seg_at(pos_n) : cur;
+  has_next = has_next && nxt.blk1 > nxt.blk0;
   int tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
   nk = chunk_blocks(cur, c0);
 
@@ -717,7 +746,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     pos = pos_n;
     pos_n = next_pos(cur, pos);
     has_next = pos_n < pos_end;
-    if (has_next) nxt = seg_at(pos_n);
+    if (has_next) {
+      nxt = seg_at(pos_n);
+      has_next = nxt.blk1 > nxt.blk0;
+    }
     tbl = tbl_nxt;
     load_q(cur, qv);
     tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
@@ -744,7 +776,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   if (pa_s >= 0 || pb_s >= 0) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    auto pair_start = [&](int q, int g) { return Hkv * sm_pre[q] + g * nb_of(q); };
+    // work position of the pair's block 0; its work range starts C earlier
+    auto pair_start = [&](int q, int g) { return Hkv * sm_pre[q] + g * cost_of(q) + C; };
     auto pieces = [&](int q, int g) {
       const int A = pair_start(q, g);
       return (A + nb_of(q) - 1) / Q - A / Q + 1;
@@ -763,14 +796,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (sm_last[0]) {
       const int A = pair_start(pa_s, pa_g);
-      merge_pair<T, D, N>(a, pa_s, pa_g, A, A + nb_of(pa_s), Q, tid);
+      merge_pair<T, D, N, kThreads>(a, pa_s, pa_g, A - C, A, A + nb_of(pa_s), Q, tid);
       if (tid == 0)
         __hip_atomic_store(a.counters + pa_s * Hkv + pa_g, 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     if (sm_last[1]) {
       const int A = pair_start(pb_s, pb_g);
-      merge_pair<T, D, N>(a, pb_s, pb_g, A, A + nb_of(pb_s), Q, tid);
+      merge_pair<T, D, N, kThreads>(a, pb_s, pb_g, A - C, A, A + nb_of(pb_s), Q, tid);
       if (tid == 0)
         __hip_atomic_store(a.counters + pb_s * Hkv + pb_g, 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -785,6 +818,7 @@ hipError_t run_typed(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = plan_lds_bytes(a.num_seqs);
   const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R>);
   int resident = 0;
+  constexpr int kThreads = 64 * decode_waves<T, D, R>();
   hipError_t e = resident_workgroups(fn, kThreads, lds, &resident);
   if (e != hipSuccess) return e;
   const int64_t work = a.min_slice_blocks > 0

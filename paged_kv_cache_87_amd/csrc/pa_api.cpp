@@ -205,6 +205,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max
   if (partition_size <= 0 || partition_size >= cover) return p;   // no split
   p.min_slice_blocks = partition_size / kBlockSize;
   const int64_t slices = (p.max_blocks + p.min_slice_blocks - 1) / p.min_slice_blocks;
+  p.max_blocks += static_cast<int64_t>(num_kv_heads) * num_seqs * kSegCost;   // work range
   p.max_slices = static_cast<int32_t>(slices < kMaxSlices ? (slices > 0 ? slices : 1)
                                                           : kMaxSlices);
   const size_t rows = static_cast<size_t>(2) * p.max_slices * (num_q_heads / num_kv_heads);
@@ -408,6 +409,7 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   a.context_cap = plan.context_cap;
   a.min_slice_blocks = plan.min_slice_blocks;
   a.max_slices = plan.max_slices;
+  a.seg_cost = plan.min_slice_blocks > 0 ? pa::kSegCost : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.geom = geom_of(pool);
   return hip_status(pa::launch_decode(a, stream), "decode launch");

@@ -90,6 +90,7 @@ struct DecodeArgs {
   int32_t context_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
   int32_t min_slice_blocks;  // 0: every (sequence, KV head) in one pass; else split
   int32_t max_slices;      // split: upper bound of the grid (partial slots = 2x)
+  int32_t seg_cost;        // split: price of a segment's fixed cost, in blocks
   float scale_log2;        // softmax scale * log2(e)
   PoolGeom geom;
 };
@@ -136,6 +137,9 @@ constexpr int kCounterSlots = 65536;
 constexpr size_t kCounterHeaderBytes = kCounterSlots * sizeof(int32_t);
 // At most this many slices (workgroups) share a split decode.
 constexpr int kMaxSlices = 2048;
+// A split decode prices each (sequence, KV head) segment at this many blocks
+// on top of its blocks when it cuts the work into equal slices.
+constexpr int kSegCost = 24;
 
 // Split plan shared by the workspace query and pa_decode.
 struct DecodePlan {
@@ -145,7 +149,7 @@ struct DecodePlan {
   size_t workspace_bytes;
   size_t part_o_offset;      // byte offsets inside the workspace
   size_t part_ml_offset;
-  int64_t max_blocks;        // num_kv_heads * num_seqs * ceil(context_cap / block size)
+  int64_t max_blocks;        // num_kv_heads * num_seqs * (ceil(context_cap / block size) + segment price)
 };
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
                        int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
