@@ -12,8 +12,10 @@
 //   columns 32w .. 32w+31.
 //   The keys are walked in tiles of 64 (four 16-token blocks, each found
 //   through the block table) up to the tile's last position; K and V are
-//   staged in LDS as [key][d] rows, double-buffered, with the block ids of
-//   the tile after next loaded while the next tile's K/V are in flight.
+//   staged in LDS as [key][d] rows, double-buffered: at the start of a tile
+//   the next tile's K/V (loaded during the previous tile) are stashed and
+//   the loads of the tile after that are issued, so every load has a whole
+//   tile of math to arrive.
 //
 // Arithmetic (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
 //   S^T = K . Q^T   : keys on the M axis, the wave's 32 columns on N; the
@@ -199,15 +201,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   if (n_kt > 0) {
     load_ids(0, ids);
     fetch(0, ids);
-    if (n_kt > 1) load_ids(1, ids);
     stash(0);
+    if (n_kt > 1) {
+      load_ids(1, ids);
+      fetch(1, ids);
+      if (n_kt > 2) load_ids(2, ids);
+    }
   }
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
+    // Tile kt + 1 was fetched at the start of the previous tile: stash it
+    // first (buffer buf^1 was last read before the previous barrier), then
+    // issue tile kt + 2's loads into the same registers.  With the stash
+    // ahead of the new loads, its wait covers only loads a whole tile old.
     if (kt + 1 < n_kt) {
-      fetch(kt + 1, ids);               // next tile's loads fly during this tile's math
-      if (kt + 2 < n_kt) load_ids(kt + 2, ids);
+      stash(buf ^ 1);
+      if (kt + 2 < n_kt) {
+        fetch(kt + 2, ids);
+        if (kt + 3 < n_kt) load_ids(kt + 3, ids);
+      }
     }
 
     // ---- S^T = K . Q^T for both 32-key halves first, so the second half's
@@ -280,8 +293,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    // buffer buf^1 was last read in the previous tile, before its barrier
-    if (kt + 1 < n_kt) stash(buf ^ 1);
     __syncthreads();
   }
 
