@@ -4,7 +4,8 @@
 // prefill, all prompt positions in a single kernel call; "Online Softmax").
 //
 // Work decomposition
-//   grid (query tile, kv_head, sequence), 256 threads = 4 waves.  A tile has
+//   a grid of at least one workgroup per (query tile, KV head, sequence),
+//   mapped to tiles die by die (see the kernel), 256 threads = 4 waves.  A tile has
 //   128 columns = (query head of the GQA group, token) pairs: 128 / n_rep
 //   consecutive new tokens of the sequence times the n_rep query heads that
 //   share the KV head (GQA, nanoserve Day 19 "What I learned" item 4), so a
@@ -83,9 +84,60 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int TQ = kCols / NREP;    // tokens per tile
   __shared__ PrefillSmem sm;
 
-  const int s = blockIdx.z;
-  const int g = blockIdx.y;
   const int tid = threadIdx.x;
+  // ---- which tile: the dies take (sequence, KV head) pairs round-robin -------
+  // Workgroups are handed to the eight dies (XCDs) round-robin by linear id,
+  // so linear id i runs on die i mod 8.  Die x works through the pairs x,
+  // x + 8, x + 16, ... one after the other, each pair's tiles heaviest first:
+  // every tile of a pair then runs on the die whose L2 already holds the
+  // pair's K/V, and with eight KV heads each die gets one head of every
+  // sequence, the same work.  The grid is an upper bound; surplus workgroups
+  // find no tile and leave.
+  __shared__ int sm_scan[kPThreads];
+  __shared__ int sm_pick[3];
+  {
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int die = lin & 7;
+    const int want = lin >> 3;                    // index in this die's queue of tiles
+    const int npairs = a.num_seqs * a.num_kv_heads;
+    const int mine = (npairs - die + 7) / 8;      // pairs die, die + 8, ...
+    if (tid == 0) sm_pick[0] = -1;
+    __syncthreads();
+    int base = 0;                                 // tiles of the die's earlier chunks
+    for (int c0 = 0; c0 < mine; c0 += kPThreads) {
+      int nt = 0;
+      if (c0 + tid < mine) {
+        const int ss = (die + 8 * (c0 + tid)) / a.num_kv_heads;
+        int ql = a.q_start_loc[ss + 1] - a.q_start_loc[ss];
+        int LL = a.context_lens[ss];
+        LL = LL < 0 ? 0 : (LL > a.context_cap ? a.context_cap : LL);
+        ql = ql < 0 ? 0 : (ql > a.max_q_len ? a.max_q_len : ql);
+        nt = (min(ql, LL) + TQ - 1) / TQ;
+      }
+      // inclusive scan of the chunk's tile counts (Hillis-Steele in LDS)
+      sm_scan[tid] = nt;
+      __syncthreads();
+      for (int off = 1; off < kPThreads; off <<= 1) {
+        const int y = tid >= off ? sm_scan[tid - off] : 0;
+        __syncthreads();
+        sm_scan[tid] += y;
+        __syncthreads();
+      }
+      const int incl = base + sm_scan[tid];
+      if (nt > 0 && want < incl && want >= incl - nt) {
+        const int p = die + 8 * (c0 + tid);
+        sm_pick[0] = p / a.num_kv_heads;
+        sm_pick[1] = p - sm_pick[0] * a.num_kv_heads;
+        sm_pick[2] = want - (incl - nt);            // place among the pair's tiles
+      }
+      base += sm_scan[kPThreads - 1];
+      __syncthreads();
+      if (sm_pick[0] >= 0 || want < base) break;
+    }
+  }
+  if (sm_pick[0] < 0) return;
+  const int s = sm_pick[0];
+  const int g = sm_pick[1];
   const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;         // lane half: rows 4*half.. of each 8-row group
@@ -98,8 +150,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   q_len = q_len < 0 ? 0 : (q_len > a.max_q_len ? a.max_q_len : q_len);
   if (q_len > L) q_len = L;  // queries without a position in the context are skipped
   const int n_tiles = (q_len + TQ - 1) / TQ;
-  // heaviest tiles (latest tokens, most keys) are launched first
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);
+  const int tile = n_tiles - 1 - sm_pick[2];      // heaviest tiles (most keys) first
   if (tile < 0) return;
   const int t0 = tile * TQ;
   const int first_pos = L - q_len;    // position of new token 0
