@@ -18,6 +18,7 @@ the block swap between the device pool and a pinned host pool.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
+    python bench.py --prefill-only       # the batched prefill alone, for its counters
 """
 
 from __future__ import annotations
@@ -57,6 +58,8 @@ def parse():
                    help="every context at this length instead of uniform [1, 8192]")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain device copies of 1 GiB (HBM counter calibration)")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only run the batched prefill (for its matrix-core counters)")
     return p.parse_args()
 
 
@@ -257,6 +260,16 @@ def secondary(torch, np, stream, K, W, partition_size):
         "pcie5_x16_peak_GBps": PCIE5_X16_GBPS,
     }
     del hk, hv
+    # context for the HBM fraction: a plain 1 GiB device copy (1 GiB read + 1 GiB
+    # written) through Tensor.copy_, the ceiling a streaming kernel meets here
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    _, cp_ms = timed(torch, stream, K, W, lambda: None, lambda: b.copy_(a))
+    out["hbm_copy_ceiling"] = {"bytes_moved": 2 << 30,
+                               "GBps": (2 << 30) / (float(np.mean(cp_ms)) * 1e-3) / 1e9}
+    out["hbm_copy_ceiling"]["frac_hbm_peak"] = out["hbm_copy_ceiling"]["GBps"] / HBM_PEAK_GBPS
+    del a, b
     return out
 
 
@@ -292,6 +305,19 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.prefill_only:
+        w = wl.batched_prefill(pool_fill="zero")
+        g = runner.GpuStep(w)
+        g.write_history()
+        g.slot_mapping()
+        g.write()
+        _, pre_ms = timed(torch, torch.cuda.current_stream(), args.steps, args.warmup,
+                          lambda: None, g.attend)
+        lens = w.context_lens.astype(np.int64)
+        flops = 2.0 * w.num_q_heads * w.head_dim * float(np.sum(lens * (lens + 1)))
+        print(json.dumps({"prefill_us": float(np.mean(pre_ms)) * 1e3, "flops": flops,
+                          "tflops": flops / (float(np.mean(pre_ms)) * 1e-3) / 1e12}), flush=True)
         return
 
     w = wl.llama_gqa_decode(pool_fill="zero", partition_size=args.partition_size,

@@ -14,6 +14,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -239,6 +240,7 @@ class SeqDesc:
 def pa_slot_mapping(pool: KVPool, seqs: SeqDesc, slot_mapping: torch.Tensor,
                     q_start_loc: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     lib = load_library()
+    _validate_seqs(pool, seqs)
     qsl = 0 if q_start_loc is None else _dev(q_start_loc, "q_start_loc", torch.int32)
     cp, cs = pool.c(), seqs.c()
     st = lib.pa_slot_mapping(ctypes.byref(cp), ctypes.byref(cs), qsl or None,
@@ -248,9 +250,59 @@ def pa_slot_mapping(pool: KVPool, seqs: SeqDesc, slot_mapping: torch.Tensor,
     return slot_mapping
 
 
+# ---- optional contract checks (PA_VALIDATE=1) ---------------------------------
+# The library never reads device arrays on the host: a table entry or a slot
+# outside the pool is skipped by the kernels, a context length above the
+# bound is truncated.  With PA_VALIDATE=1 in the environment the binding
+# copies the tables, lengths and slots to the host before each call and
+# raises PagedAttentionError on a contract violation instead (a debugging
+# aid: it synchronises the device).
+
+def validating() -> bool:
+    return os.environ.get("PA_VALIDATE", "") == "1"
+
+
+def check_tables(block_tables, context_lens, num_blocks: int, max_context_len: int,
+                 block_size: int = 16) -> None:
+    """Raise PagedAttentionError unless every length lies in [0, min(bound,
+    table width * block_size)] and every entry a sequence reads names a block
+    of the pool.  Arrays may be numpy or torch (any device)."""
+    bt = block_tables.cpu().numpy() if isinstance(block_tables, torch.Tensor) else block_tables
+    cl = context_lens.cpu().numpy() if isinstance(context_lens, torch.Tensor) else context_lens
+    width = bt.shape[1]
+    for s, L in enumerate(cl.tolist()):
+        if L < 0 or L > max_context_len or L > width * block_size:
+            raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
+                                      f"context_lens[{s}] = {L} outside [0, {min(max_context_len, width * block_size)}]")
+        used = bt[s, :(L + block_size - 1) // block_size]
+        bad = (used < 0) | (used >= num_blocks)
+        if bad.any():
+            j = int(bad.argmax())
+            raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
+                                      f"block_tables[{s}][{j}] = {int(used[j])} is not a block of the pool")
+
+
+def check_slots(slot_mapping, num_blocks: int, block_size: int = 16) -> None:
+    """Raise PagedAttentionError if a slot (other than a negative padding
+    entry) is outside the pool or two tokens share one."""
+    sl = slot_mapping.cpu().numpy() if isinstance(slot_mapping, torch.Tensor) else slot_mapping
+    live = sl[sl >= 0]
+    if (live >= num_blocks * block_size).any():
+        raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG, "a slot lies outside the pool")
+    if len(np.unique(live)) != len(live):
+        raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG, "two tokens map to the same slot")
+
+
+def _validate_seqs(pool: KVPool, seqs: "SeqDesc") -> None:
+    if validating():
+        check_tables(seqs.block_tables, seqs.context_lens, pool.num_blocks, seqs.max_context_len)
+
+
 def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
                 slot_mapping: torch.Tensor, stream=None) -> None:
     lib = load_library()
+    if validating():
+        check_slots(slot_mapping, pool.num_blocks)
     _, _, H, D, _ = _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)
     T = slot_mapping.numel()
     for name, t in (("k_new", k_new), ("v_new", v_new)):
@@ -283,6 +335,7 @@ def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, s
               partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
               stream=None) -> torch.Tensor:
     lib = load_library()
+    _validate_seqs(pool, seqs)
     S, Hq, D = q.shape
     if tuple(out.shape) != (S, Hq, D):
         raise ValueError("out must have q's shape")
@@ -304,6 +357,7 @@ def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
                q_start_loc: torch.Tensor, max_q_len: int, scale: float,
                stream=None) -> torch.Tensor:
     lib = load_library()
+    _validate_seqs(pool, seqs)
     T, Hq, D = q.shape
     if D != _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)[3]:
         raise ValueError("q's head_dim differs from the pool's")
@@ -393,6 +447,23 @@ def pa_copy_blocks(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=No
     _check("pa_copy_blocks", st)
 
 
+def paged_attention(pool: KVPool, seqs: SeqDesc, k: torch.Tensor, v: torch.Tensor,
+                    q: torch.Tensor, slot_mapping: torch.Tensor, scale: Optional[float] = None,
+                    partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step over the paged cache, the fused read of nanoserve Day
+    19 ("What I added today"): this step's K/V rows ``[S, Hkv, D]`` go to
+    their slots, then every query row ``[S, Hq, D]`` attends over its whole
+    history through the block table.  ``scale=None`` means 1/sqrt(head_dim).
+    Two calls on one stream (pa_write_kv, pa_decode); returns ``out``."""
+    if scale is None:
+        scale = 1.0 / float(q.shape[-1]) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    pa_write_kv(pool, k, v, slot_mapping, stream)
+    return pa_decode(pool, seqs, q, out, scale, partition_size, workspace, stream)
+
+
 def host_pool_c(k_cache: torch.Tensor, v_cache: torch.Tensor, layout: str = "token") -> PaKVPool:
     """Descriptor of a K/V pool held in pinned host memory (``pin_memory=True``
     tensors shaped as for ``KVPool``)."""
@@ -420,7 +491,8 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
     "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
-    "host_pool_c", "pa_swap_blocks", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
+    "host_pool_c", "pa_swap_blocks", "paged_attention", "check_tables", "check_slots",
+    "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
     "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",
     "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",
     "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_BLOCKS", "PA_F32", "PA_BF16",

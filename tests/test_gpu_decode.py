@@ -243,3 +243,44 @@ def test_one_workspace_serves_every_shape():
         torch.cuda.synchronize()
         assert torch.equal(g.out.view(torch.uint8), ref.view(torch.uint8)), w.name
     assert int(shared[:256 * 1024].count_nonzero()) == 0
+
+
+def test_fused_paged_attention_call():
+    """The binding's one-call step (write this step's K/V, then attend, scale
+    1/sqrt(D) by default) equals the oracle's step, bit for bit in the pools."""
+    from paged_kv_cache_87_amd import binding as pa
+    w = wl.decode_workload("fused", 37, dtype=wl.BF16, num_q_heads=16, num_kv_heads=4,
+                           head_dim=128, block_size=16, num_blocks=512,
+                           context_lens=[5, 300, 1025, 16], partition_size=256)
+    announce(w.name)
+    g = runner.GpuStep(w)
+    g.write_history()
+    g.slot_mapping()
+    out = pa.paged_attention(g.pool, g.seqs, g.new_k, g.new_v, g.q, g.slots,
+                             partition_size=256, workspace=g.workspace)
+    torch.cuda.synchronize()
+    k_ref, v_ref, _, out_ref = oracle_step(w)
+    assert_pools_equal(g, k_ref, v_ref)
+    assert w.scale == pytest.approx(1 / np.sqrt(128))
+    assert_close(out.float().cpu().numpy().astype(np.float64), out_ref, w.dtype, w.name)
+
+
+def test_validate_mode_rejects_a_bad_table(monkeypatch):
+    """With PA_VALIDATE=1 a table entry outside the pool is reported before
+    any launch; without it the kernels skip the entry."""
+    from paged_kv_cache_87_amd import binding as pa
+    w = wl.tiny_decode()
+    announce("validate mode")
+    g = runner.run_workload(w)
+    bad = g.block_tables.clone()
+    bad[0, 3] = w.num_blocks + 5
+    seqs = pa.SeqDesc(bad, g.context_lens, w.max_context_len)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    with pytest.raises(pa.PagedAttentionError):
+        pa.pa_decode(g.pool, seqs, g.q, torch.empty_like(g.q), w.scale, 0, None)
+    two_k, two_v = g.new_k.repeat(2, 1, 1), g.new_v.repeat(2, 1, 1)
+    with pytest.raises(pa.PagedAttentionError):          # two tokens, one slot
+        pa.pa_write_kv(g.pool, two_k, two_v, torch.tensor([3, 3], dtype=torch.int64, device="cuda"))
+    monkeypatch.delenv("PA_VALIDATE")
+    pa.pa_decode(g.pool, g.seqs, g.q, torch.empty_like(g.q), w.scale, 0, None)   # valid: runs
+    torch.cuda.synchronize()
