@@ -231,6 +231,22 @@ pa_status pa_allocator_prepare_write(pa_block_allocator* alloc, int32_t* table, 
                                      int32_t copy_cap, int32_t* num_copies);
 
 /*
+ * pa_append_kv -- the decode step's write in one launch: pa_slot_mapping
+ * without q_start_loc (each sequence's newest position, context_lens[s] - 1)
+ * fused with pa_write_kv (nanoserve Day 19, "What I added today": this
+ * step's K/V written to its slot before attention reads the history).
+ *
+ * k_new, v_new (device, [num_seqs, num_kv_heads, head_dim] of the pool's
+ * dtype, 16-byte aligned): row s goes to sequence s's slot, bit for bit.
+ * slot_mapping (device, int64 [num_seqs], written; may be NULL): the slot
+ * used for each sequence, -1 where it was skipped (empty context, position
+ * past the table width, or a table entry that is not a block of the pool).
+ * The result equals pa_slot_mapping followed by pa_write_kv.
+ */
+pa_status pa_append_kv(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* k_new,
+                       const void* v_new, int64_t* slot_mapping, hipStream_t stream);
+
+/*
  * pa_copy_blocks -- copy whole blocks of both pools on the device: for each
  * pair i, block src_blocks[i] of k_cache and of v_cache is copied bit for
  * bit to block dst_blocks[i] (the data move of a copy-on-write).

@@ -39,7 +39,7 @@ EXPORTED = (
     "pa_status_string", "pa_last_error", "pa_version", "pa_allocator_create",
     "pa_allocator_destroy", "pa_allocator_num_free", "pa_allocator_refcount",
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
-    "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks",
+    "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks", "pa_append_kv",
 )
 
 
@@ -105,6 +105,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_allocator_prepare_write": (i32, [vp, vp, i32, vp, i32, i32, i32, vp, vp, i32, vp]),
         "pa_copy_blocks": (i32, [pool_p, vp, vp, i32, vp]),
         "pa_swap_blocks": (i32, [pool_p, pool_p, vp, vp, i32, i32, vp]),
+        "pa_append_kv": (i32, [pool_p, seq_p, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -315,6 +316,26 @@ def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
     _check("pa_write_kv", st)
 
 
+def pa_append_kv(pool: KVPool, seqs: "SeqDesc", k_new: torch.Tensor, v_new: torch.Tensor,
+                 slot_mapping: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Slot mapping of each sequence's newest position and the K/V write, one
+    launch (``k_new``/``v_new`` ``[num_seqs, Hkv, D]``)."""
+    lib = load_library()
+    _validate_seqs(pool, seqs)
+    _, _, H, D, _ = _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)
+    S = int(seqs.block_tables.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (S, H, D):
+            raise ValueError(f"{name} must be [{S}, {H}, {D}], got {tuple(t.shape)}")
+    if slot_mapping is not None and tuple(slot_mapping.shape) != (S,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    cp, cs = pool.c(), seqs.c()
+    sm = None if slot_mapping is None else _dev(slot_mapping, "slot_mapping", torch.int64)
+    st = lib.pa_append_kv(ctypes.byref(cp), ctypes.byref(cs), _dev(k_new, "k_new", pool.dtype),
+                          _dev(v_new, "v_new", pool.dtype), sm, _stream(stream))
+    _check("pa_append_kv", st)
+
+
 def pa_decode_workspace_bytes(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
                               partition_size: int) -> int:
     cp, cs = pool.c(), seqs.c()
@@ -491,7 +512,7 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
     "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
-    "host_pool_c", "pa_swap_blocks", "paged_attention", "check_tables", "check_slots",
+    "host_pool_c", "pa_swap_blocks", "paged_attention", "pa_append_kv", "check_tables", "check_slots",
     "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
     "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",
     "pa_version", "PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED",

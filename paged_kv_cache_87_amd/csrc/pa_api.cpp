@@ -272,6 +272,24 @@ pa_status pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_n
   return hip_status(pa::launch_write_kv(a, stream), "write_kv launch");
 }
 
+pa_status pa_append_kv(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* k_new,
+                       const void* v_new, int64_t* slot_mapping, hipStream_t stream) {
+  clear_error();
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if (seqs->num_seqs == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "k_new or v_new is null");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  pa::AppendKVArgs a{k_new, v_new, pool->k_cache, pool->v_cache, seqs->block_tables,
+                     seqs->context_lens, slot_mapping, seqs->num_seqs, seqs->max_blocks_per_seq,
+                     pool->num_blocks, pool->num_kv_heads * pool->head_dim * elt_size(pool->dtype),
+                     pool->head_dim * elt_size(pool->dtype), geom_of(pool)};
+  return hip_status(pa::launch_append_kv(a, stream), "append_kv launch");
+}
+
 pa_status pa_copy_blocks(const pa_kv_pool* pool, const int32_t* src_blocks,
                          const int32_t* dst_blocks, int32_t num_pairs, hipStream_t stream) {
   clear_error();

@@ -53,6 +53,23 @@ struct WriteKVArgs {
 };
 hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream);
 
+struct AppendKVArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int64_t* slot_mapping;   // may be null
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t row_bytes;       // num_kv_heads * head_dim * element size
+  int32_t head_bytes;      // head_dim * element size
+  PoolGeom geom;
+};
+hipError_t launch_append_kv(const AppendKVArgs& a, hipStream_t stream);
+
 struct CopyBlocksArgs {
   const void* src_k;       // source pools (device or pinned host)
   const void* src_v;

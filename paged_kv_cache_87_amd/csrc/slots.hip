@@ -21,6 +21,19 @@ namespace {
 constexpr int kSlotThreads = 256;
 constexpr int kWriteThreads = 256;
 
+// Slot of position `pos` of sequence `s` whose context is `L` tokens: the
+// table's block for pos / 16, offset pos % 16; -1 when the position is not in
+// the context or the table entry is not a block of the pool.
+__device__ __forceinline__ int64_t slot_of(const int32_t* block_tables, int max_blocks_per_seq,
+                                           int num_blocks, int s, int L, int pos) {
+  if (pos < 0 || pos >= L) return -1;
+  const int logical = pos / kBlockSize;
+  if (logical >= max_blocks_per_seq) return -1;
+  const int phys = block_tables[static_cast<int64_t>(s) * max_blocks_per_seq + logical];
+  if (phys < 0 || phys >= num_blocks) return -1;
+  return static_cast<int64_t>(phys) * kBlockSize + (pos % kBlockSize);
+}
+
 __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingArgs a) {
   const int i = blockIdx.x * kSlotThreads + threadIdx.x;
   if (i >= a.num_tokens) return;
@@ -42,17 +55,10 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingA
     idx = i - a.q_start_loc[s];
   }
   const int L = a.context_lens[s];
-  const int pos = L - q_len + idx;
-  int64_t slot = -1;
-  if (idx >= 0 && idx < q_len && pos >= 0 && pos < L) {
-    const int logical = pos / kBlockSize;
-    if (logical < a.max_blocks_per_seq) {
-      const int phys = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + logical];
-      if (phys >= 0 && phys < a.num_blocks)
-        slot = static_cast<int64_t>(phys) * kBlockSize + (pos % kBlockSize);
-    }
-  }
-  a.slot_mapping[i] = slot;
+  a.slot_mapping[i] = idx >= 0 && idx < q_len
+                          ? slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks, s, L,
+                                    L - q_len + idx)
+                          : -1;
 }
 
 // One 16-byte chunk per thread; blockIdx.y selects K (0) or V (1).  The
@@ -81,7 +87,42 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) 
   *reinterpret_cast<uint4*>(dst + dst_off) = src[static_cast<int64_t>(t) * chunks_per_row + part];
 }
 
+// The decode step's write in one launch: each thread finds the slot of its
+// sequence's newest position (context_lens[s] - 1) itself and copies one
+// 16-byte chunk of that token's K (blockIdx.y 0) or V (1) row; the first
+// chunk's thread of the K pass records the slot.
+__global__ __launch_bounds__(kWriteThreads) void append_kv_kernel(AppendKVArgs a) {
+  const int chunks_per_row = a.row_bytes >> 4;
+  const int chunks_per_head = a.head_bytes >> 4;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kWriteThreads + threadIdx.x;
+  if (c >= static_cast<int64_t>(a.num_seqs) * chunks_per_row) return;
+  const int t = static_cast<int>(c / chunks_per_row);
+  const int part = static_cast<int>(c - static_cast<int64_t>(t) * chunks_per_row);
+  const int L = a.context_lens[t];
+  const int64_t slot = slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks, t, L, L - 1);
+  if (part == 0 && blockIdx.y == 0 && a.slot_mapping != nullptr) a.slot_mapping[t] = slot;
+  if (slot < 0) return;
+  const int h = part / chunks_per_head;
+  const int q = part - h * chunks_per_head;
+  const int64_t blk = slot / kBlockSize;
+  const int in_blk = static_cast<int>(slot - blk * kBlockSize);
+  const int64_t dst_off = blk * a.geom.block_stride +
+                          static_cast<int64_t>(in_blk) * a.geom.token_stride +
+                          static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;
+  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
+  char* dst = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  *reinterpret_cast<uint4*>(dst + dst_off) = src[static_cast<int64_t>(t) * chunks_per_row + part];
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(const AppendKVArgs& a, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.num_seqs) * (a.row_bytes >> 4);
+  const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
+  hipLaunchKernelGGL(append_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t stream) {
   const int grid = (a.num_tokens + kSlotThreads - 1) / kSlotThreads;

@@ -143,6 +143,10 @@ class GpuStep:
     def write(self):
         pa.pa_write_kv(self.pool, self.new_k, self.new_v, self.slots)
 
+    def append(self):
+        """Decode step's slot mapping and write in one launch."""
+        pa.pa_append_kv(self.pool, self.seqs, self.new_k, self.new_v, self.slots)
+
     def attend(self, partition_size=None):
         w = self.w
         if w.kind == "decode":

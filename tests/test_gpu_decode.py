@@ -284,3 +284,24 @@ def test_validate_mode_rejects_a_bad_table(monkeypatch):
     monkeypatch.delenv("PA_VALIDATE")
     pa.pa_decode(g.pool, g.seqs, g.q, torch.empty_like(g.q), w.scale, 0, None)   # valid: runs
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype,layout", [(wl.BF16, "token"), (wl.F32, "head"),
+                                          (wl.BF16, "unified_token")])
+def test_append_equals_slot_mapping_then_write(dtype, layout):
+    """The fused decode-step write gives the oracle's slots and pools, bit for
+    bit, including sequences whose slot is skipped (empty context)."""
+    w = wl.decode_workload("append", 38, dtype=dtype, num_q_heads=8, num_kv_heads=4,
+                           head_dim=64 if dtype == wl.F32 else 128, block_size=16,
+                           num_blocks=256, context_lens=[1, 16, 17, 0, 300, 1025],
+                           partition_size=0)
+    announce(f"{w.name} {dtype} {layout}")
+    g = runner.GpuStep(w, layout=layout)
+    g.write_history()
+    g.append()
+    g.attend()
+    torch.cuda.synchronize()
+    k_ref, v_ref, slots_ref, out_ref = oracle_step(w)
+    assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
+    assert_pools_equal(g, k_ref, v_ref)
+    assert_close(g.out_f64(), out_ref, w.dtype, w.name)
