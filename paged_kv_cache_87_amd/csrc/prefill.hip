@@ -11,12 +11,15 @@
 //   share the KV head (GQA, nanoserve Day 19 "What I learned" item 4), so a
 //   K/V tile brought into LDS serves every head of the group.  Wave w owns
 //   columns 32w .. 32w+31.
-//   The keys are walked in tiles of 64 (four 16-token blocks, each found
+//   The keys are walked in tiles of 32 (two 16-token blocks, each found
 //   through the block table) up to the tile's last position; K and V are
 //   staged in LDS as [key][d] rows, double-buffered: at the start of a tile
 //   the next tile's K/V (loaded during the previous tile) are stashed and
 //   the loads of the tile after that are issued, so every load has a whole
-//   tile of math to arrive.
+//   tile of math to arrive.  32-key tiles keep the kernel at 154 VGPRs and
+//   37 KB of LDS, so three workgroups (three waves per SIMD) share a CU; with
+//   64-key tiles it needed 198 VGPRs and 70 KB, two per CU, and ran ~6 %
+//   slower.
 //
 // Arithmetic (v_mfma_f32_32x32x16_bf16, fp32 accumulation)
 //   S^T = K . Q^T   : keys on the M axis, the wave's 32 columns on N; the
@@ -48,7 +51,8 @@ constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kD = 128;               // head_dim handled here
 constexpr int kCols = 128;            // (head, token) columns per workgroup
-constexpr int kKeys = 64;             // keys per K/V tile (4 blocks)
+constexpr int kKeys = 32;             // keys per K/V tile (2 blocks)
+constexpr int kHalves = kKeys / 32;   // 32-key halves per tile = loader passes
 constexpr int kKStride = kD + 8;      // LDS row stride of K (bf16 elements): 68 dwords
 constexpr int kVStride = kD + 16;     // ... of V: 72 dwords, conflict-free transposing reads
 constexpr float kPNegBig = -1.0e30f;
@@ -184,8 +188,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const uint32_t row_bytes = a.geom.token_stride;     // next token row of one KV head
   const uint32_t block_bytes = a.geom.span;           // a block's rows (both layouts)
 
-  // ---- K/V tile loader: 64 keys x 128 d, K and V as [key][d] rows -----------
-  // thread -> (key pair 8 w + 2 (lane / 16) (+32 for the second pass), d chunk
+  // ---- K/V tile loader: kKeys keys x 128 d, K and V as [key][d] rows --------
+  // thread -> (key pair 8 w + 2 (lane / 16) (+32 per further pass), d chunk
   // dc = lane % 16): the keys of one wave and pass lie in one 16-token block,
   // so its block id is wave-uniform and the loads go through a buffer
   // descriptor; keys past the context read as zeros (offset past the
@@ -195,17 +199,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
-  auto load_ids = [&](int kt, int (&ids)[2]) {
+  auto load_ids = [&](int kt, int (&ids)[kHalves]) {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
+    for (int ps = 0; ps < kHalves; ++ps) {
       const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;   // the wave's first key this pass
       ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
     }
   };
-  uint4 kreg[2][2], vreg[2][2];       // [pass][key of the pair]
-  auto fetch = [&](int kt, const int (&ids)[2]) {
+  uint4 kreg[kHalves][2], vreg[kHalves][2];  // [pass][key of the pair]
+  auto fetch = [&](int kt, const int (&ids)[kHalves]) {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
+    for (int ps = 0; ps < kHalves; ++ps) {
       const int phys = uniform(ids[ps]);
       const bool ok = phys >= 0 && phys < a.num_blocks;
       const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
+    for (int ps = 0; ps < kHalves; ++ps)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int key = ld_key + 32 * ps + e;
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // the tile's smallest query position: key tiles up to it need no mask
   const int min_qpos = first_pos + t0;
 
-  int ids[2];
+  int ids[kHalves];
   if (n_kt > 0) {
     load_ids(0, ids);
     fetch(0, ids);
@@ -274,11 +278,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- S^T = K . Q^T for both 32-key halves first, so the second half's
-    // matrix work runs while the first half's softmax is on the VALU ---------
-    f32x16 st[2];
+    // ---- S^T = K . Q^T for every 32-key half of the tile first (with 64-key
+    // tiles the second half's matrix work then runs under the first half's
+    // softmax) -----------------------------------------------------------------
+    f32x16 st[kHalves];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kHalves; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
 #pragma unroll
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
     // ---- per half: causal mask, online softmax, O^T += V^T . P^T ------------
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kHalves; ++t) {
       // causal mask only where the half reaches past a position; lanes of
       // invalid columns compute values that are never stored
       const int key0 = kt * kKeys + 32 * t;
