@@ -58,6 +58,18 @@ def test_prefill_chunked_continuation(n_rep):
     _full(w)
 
 
+@pytest.mark.parametrize("n_rep", [2, 4])
+def test_prefill_key_tile_edges(n_rep):
+    """Contexts, and first positions of continued prompts, on both sides of the
+    32-key tile and 32-token query tile edges."""
+    w = wl.prefill_workload(f"prefill_edges_r{n_rep}", 620 + n_rep, dtype=wl.BF16,
+                            num_q_heads=2 * n_rep, num_kv_heads=2, head_dim=128, block_size=16,
+                            num_blocks=512,
+                            context_lens=[31, 32, 33, 63, 96, 97, 100, 100, 100, 129],
+                            q_lens=[31, 32, 33, 63, 96, 97, 68, 69, 67, 33])
+    _full(w)
+
+
 def test_prefill_batched_full_size_sampled():
     """16 prompts of U[256, 2048] tokens, 32/8 heads: every pool byte, and
     sampled output rows (first, last and random tokens of every prompt)."""
