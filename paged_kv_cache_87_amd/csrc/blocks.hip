@@ -43,9 +43,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
 }  // namespace
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2, kCopySplit), dim3(kCopyThreads), 0,
-                     stream, a);
-  return hipGetLastError();
+  return launch_kernel(copy_blocks_kernel, dim3(a.num_pairs, 2, kCopySplit), dim3(kCopyThreads), 0,
+                       stream, a);
 }
 
 }  // namespace pa

@@ -825,8 +825,7 @@ hipError_t run_typed(const DecodeArgs& a, hipStream_t stream) {
                            ? static_cast<int64_t>(a.max_slices)
                            : static_cast<int64_t>(a.num_kv_heads) * a.num_seqs;
   const int grid = static_cast<int>(resident < work ? resident : (work > 0 ? work : 1));
-  hipLaunchKernelGGL((decode_kernel<T, D, R>), dim3(grid), dim3(kThreads), lds, stream, a);
-  return hipGetLastError();
+  return launch_kernel(decode_kernel<T, D, R>, dim3(grid), dim3(kThreads), lds, stream, a);
 }
 
 template <typename T, int D>

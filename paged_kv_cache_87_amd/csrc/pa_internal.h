@@ -10,6 +10,17 @@
 
 namespace pa {
 
+// Launch kernel(a) and return this launch's own status.  hipLaunchKernel
+// reports only its own error; hipGetLastError after a hipLaunchKernelGGL
+// would also return an earlier failure of some unrelated HIP call the caller
+// made and did not clear, and blame it on the launch.
+template <typename A>
+inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, const A& a) {
+  void* args[] = {const_cast<A*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, stream);
+}
+
 // Thread-local error text behind pa_last_error(): clear at entry, set with
 // the failing status (returned unchanged).
 void clear_report();

@@ -377,13 +377,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int tiles = (a.max_q_len + tq - 1) / tq;
   dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
   switch (n_rep) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<0>, grid, dim3(kPThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<3>, grid, dim3(kPThreads), 0, stream, a); break;
+    case 1: return launch_kernel(prefill_kernel<0>, grid, dim3(kPThreads), 0, stream, a);
+    case 2: return launch_kernel(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, a);
+    case 4: return launch_kernel(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, a);
+    case 8: return launch_kernel(prefill_kernel<3>, grid, dim3(kPThreads), 0, stream, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pa

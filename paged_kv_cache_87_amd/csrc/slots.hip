@@ -73,6 +73,9 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) 
   if (c >= total) return;
   const int t = static_cast<int>(c / chunks_per_row);
   const int part = static_cast<int>(c - static_cast<int64_t>(t) * chunks_per_row);
+  // the source chunk does not depend on the slot: its load overlaps the slot's
+  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
+  const uint4 val = src[static_cast<int64_t>(t) * chunks_per_row + part];
   const int64_t slot = a.slot_mapping[t];
   if (slot < 0 || slot >= a.num_slots) return;
   const int h = part / chunks_per_head;
@@ -82,9 +85,8 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) 
   const int64_t dst_off = blk * a.geom.block_stride +
                           static_cast<int64_t>(in_blk) * a.geom.token_stride +
                           static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;
-  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
   char* dst = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
-  *reinterpret_cast<uint4*>(dst + dst_off) = src[static_cast<int64_t>(t) * chunks_per_row + part];
+  *reinterpret_cast<uint4*>(dst + dst_off) = val;
 }
 
 // The decode step's write in one launch: each thread finds the slot of its
@@ -98,6 +100,10 @@ __global__ __launch_bounds__(kWriteThreads) void append_kv_kernel(AppendKVArgs a
   if (c >= static_cast<int64_t>(a.num_seqs) * chunks_per_row) return;
   const int t = static_cast<int>(c / chunks_per_row);
   const int part = static_cast<int>(c - static_cast<int64_t>(t) * chunks_per_row);
+  // the source chunk does not depend on the slot: its load overlaps the two
+  // dependent loads (context length, table entry) that find the slot
+  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
+  const uint4 val = src[static_cast<int64_t>(t) * chunks_per_row + part];
   const int L = a.context_lens[t];
   const int64_t slot = slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks, t, L, L - 1);
   if (part == 0 && blockIdx.y == 0 && a.slot_mapping != nullptr) a.slot_mapping[t] = slot;
@@ -109,9 +115,8 @@ __global__ __launch_bounds__(kWriteThreads) void append_kv_kernel(AppendKVArgs a
   const int64_t dst_off = blk * a.geom.block_stride +
                           static_cast<int64_t>(in_blk) * a.geom.token_stride +
                           static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;
-  const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
   char* dst = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
-  *reinterpret_cast<uint4*>(dst + dst_off) = src[static_cast<int64_t>(t) * chunks_per_row + part];
+  *reinterpret_cast<uint4*>(dst + dst_off) = val;
 }
 
 }  // namespace
@@ -119,23 +124,20 @@ __global__ __launch_bounds__(kWriteThreads) void append_kv_kernel(AppendKVArgs a
 hipError_t launch_append_kv(const AppendKVArgs& a, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(a.num_seqs) * (a.row_bytes >> 4);
   const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
-  hipLaunchKernelGGL(append_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
-                     stream, a);
-  return hipGetLastError();
+  return launch_kernel(append_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
+                       stream, a);
 }
 
 hipError_t launch_slot_mapping(const SlotMappingArgs& a, hipStream_t stream) {
   const int grid = (a.num_tokens + kSlotThreads - 1) / kSlotThreads;
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(kSlotThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(slot_mapping_kernel, dim3(grid), dim3(kSlotThreads), 0, stream, a);
 }
 
 hipError_t launch_write_kv(const WriteKVArgs& a, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(a.num_tokens) * (a.row_bytes >> 4);
   const int64_t grid = (total + kWriteThreads - 1) / kWriteThreads;
-  hipLaunchKernelGGL(write_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
-                     stream, a);
-  return hipGetLastError();
+  return launch_kernel(write_kv_kernel, dim3(static_cast<unsigned>(grid), 2), dim3(kWriteThreads), 0,
+                       stream, a);
 }
 
 }  // namespace pa

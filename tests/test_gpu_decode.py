@@ -305,3 +305,29 @@ def test_append_equals_slot_mapping_then_write(dtype, layout):
     assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
     assert_pools_equal(g, k_ref, v_ref)
     assert_close(g.out_f64(), out_ref, w.dtype, w.name)
+
+
+def test_unrelated_hip_error_is_not_blamed_on_a_launch():
+    """A failed HIP call of the caller's, left uncleared, must not make the
+    next library call report a launch failure: every launch reports its own
+    status.  The stale error is a host-side invalid-device error."""
+    import ctypes
+    w = wl.decode_workload("stale_error", 41, dtype=wl.BF16, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, block_size=16, num_blocks=128,
+                           context_lens=[3, 70, 200], partition_size=64)
+    announce(w.name)
+    path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+    hip = ctypes.CDLL(path)
+    g = runner.GpuStep(w, partition_size=64)
+    g.write_history()
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0   # leaves a last error behind
+    try:
+        g.append()
+        g.attend()
+        torch.cuda.synchronize()
+    finally:
+        hip.hipGetLastError()
+    k_ref, v_ref, _, out_ref = oracle_step(w)
+    assert_pools_equal(g, k_ref, v_ref)
+    assert_close(g.out_f64(), out_ref, w.dtype, w.name)
