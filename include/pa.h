@@ -15,6 +15,10 @@
  *   descriptor structs themselves) are only read during the call.
  * - Work is enqueued on `stream` (NULL = the default stream) and runs
  *   asynchronously; a PA_OK return means the launch was accepted.
+ *   PA_ERR_HIP carries the HIP status of the library's own launch only: an
+ *   earlier failed HIP call of the caller's, left uncleared, neither fails a
+ *   call here nor is cleared by one.  Faults during execution surface at the
+ *   caller's next synchronisation, as for any HIP kernel.
  * - Arguments are checked on the host before anything is enqueued.  A
  *   failed check returns PA_ERR_INVALID_ARG or PA_ERR_UNSUPPORTED and
  *   enqueues nothing; pa_last_error() then describes the failed check.
