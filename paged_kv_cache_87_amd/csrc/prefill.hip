@@ -4,8 +4,9 @@
 // prefill, all prompt positions in a single kernel call; "Online Softmax").
 //
 // Work decomposition
-//   a grid of at least one workgroup per (query tile, KV head, sequence),
-//   mapped to tiles die by die (see the kernel), 256 threads = 4 waves.  A tile has
+//   a one-dimensional grid, 8 x ceil(pairs / 8) x (query tiles of the
+//   longest prompt) workgroups, mapped to (query tile, KV head, sequence)
+//   die by die (see the kernel), 256 threads = 4 waves.  A tile has
 //   128 columns = (query head of the GQA group, token) pairs: 128 / n_rep
 //   consecutive new tokens of the sequence times the n_rep query heads that
 //   share the KV head (GQA, nanoserve Day 19 "What I learned" item 4), so a
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ int sm_scan[kPThreads];
   __shared__ int sm_pick[3];
   {
-    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int lin = blockIdx.x;
     const int die = lin & 7;
     const int want = lin >> 3;                    // index in this die's queue of tiles
     const int npairs = a.num_seqs * a.num_kv_heads;
@@ -374,8 +375,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int n_rep = a.num_q_heads / a.num_kv_heads;
   const int tq = kCols / n_rep;
-  const int tiles = (a.max_q_len + tq - 1) / tq;
-  dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
+  const int64_t tiles = (a.max_q_len + tq - 1) / tq;
+  // Die x (workgroups x, x + 8, ...) serves the pairs x, x + 8, ...: at most
+  // ceil(pairs / 8) pairs of at most `tiles` tiles each, so every die needs
+  // that many workgroups of its own, whatever the pair count mod 8.
+  const int64_t pairs = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  const int64_t per_die = (pairs + 7) / 8 * tiles;
+  if (per_die <= 0) return hipSuccess;
+  if (8 * per_die > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(8 * per_die));
   switch (n_rep) {
     case 1: return launch_kernel(prefill_kernel<0>, grid, dim3(kPThreads), 0, stream, a);
     case 2: return launch_kernel(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, a);

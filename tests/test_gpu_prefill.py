@@ -70,6 +70,21 @@ def test_prefill_key_tile_edges(n_rep):
     _full(w)
 
 
+@pytest.mark.parametrize("num_kv_heads,context_lens", [
+    (2, [37, 70]),                      # 4 (sequence, KV head) pairs: half the dies idle
+    (1, [120, 507, 460, 483, 667]),     # 5 pairs of unequal tile counts
+    (4, [300, 65, 290]),                # 12 pairs: dies 0-3 serve two pairs, 4-7 one
+])
+def test_prefill_pair_count_not_multiple_of_eight(num_kv_heads, context_lens):
+    """Every query tile is computed when the (sequence, KV head) pairs do not
+    split evenly over the eight dies the tiles are queued by."""
+    w = wl.prefill_workload(f"prefill_pairs_h{num_kv_heads}_s{len(context_lens)}",
+                            630 + num_kv_heads, dtype=wl.BF16, num_q_heads=4 * num_kv_heads,
+                            num_kv_heads=num_kv_heads, head_dim=128, block_size=16,
+                            num_blocks=256, context_lens=context_lens)
+    _full(w)
+
+
 def test_prefill_batched_full_size_sampled():
     """16 prompts of U[256, 2048] tokens, 32/8 heads: every pool byte, and
     sampled output rows (first, last and random tokens of every prompt)."""
