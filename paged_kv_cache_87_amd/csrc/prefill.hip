@@ -275,7 +275,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       stash(buf ^ 1);
       if (kt + 2 < n_kt) {
         fetch(kt + 2, ids);
-        if (kt + 3 < n_kt) load_ids(kt + 3, ids);
       }
     }
 
@@ -320,14 +319,18 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       }
-      // P^T in bf16, packed straight from the accumulator layout
+      // P^T in bf16, packed straight from the accumulator layout; the running
+      // sum adds the same rounded values the P.V product weights V by (one
+      // v_dot2_f32_bf16 against (1, 1) per pair), so the normalised output is
+      // a convex combination of the V rows
       uint32_t pk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(st[t][r], sl2, -m));
         const float p1 = fast_exp2(fmaf(st[t][r + 1], sl2, -m));
-        lsum += p0 + p1;
         pk[r >> 1] = pack_bf16(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r >> 1]),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), lsum, false);
       }
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
@@ -350,6 +353,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+    // block ids two tiles ahead: read from the table after the products, so the
+    // scalar load's wait does not hold up the K fragment reads of this tile
+    if (kt + 3 < n_kt) load_ids(kt + 3, ids);
     __syncthreads();
   }
 
