@@ -85,6 +85,25 @@ def test_prefill_pair_count_not_multiple_of_eight(num_kv_heads, context_lens):
     _full(w)
 
 
+@pytest.mark.parametrize("num_seqs,num_kv_heads,hi", [
+    (64, 8, 300),     # 64 (sequence, KV head) pairs per die
+    (520, 1, 40),     # 65 pairs per die, one KV head
+    (2100, 1, 12),    # 263 pairs per die: the tile scan takes two 256-pair chunks
+])
+def test_prefill_many_pairs_per_die(num_seqs, num_kv_heads, hi):
+    """Every tile is computed when the dies' tile queues hold many pairs, with
+    many equal prompt lengths."""
+    rng = np.random.default_rng(650 + num_kv_heads)
+    lens = rng.integers(1, hi + 1, size=num_seqs)
+    lens[::5] = hi // 2
+    nb = int(sum((int(x) + 15) // 16 for x in lens)) + 8
+    w = wl.prefill_workload(f"prefill_many_pairs_s{num_seqs}_h{num_kv_heads}", 650 + num_kv_heads,
+                            dtype=wl.BF16, num_q_heads=4 * num_kv_heads, num_kv_heads=num_kv_heads,
+                            head_dim=128, block_size=16, num_blocks=nb,
+                            context_lens=[int(x) for x in lens])
+    _full(w)
+
+
 def test_prefill_batched_full_size_sampled():
     """16 prompts of U[256, 2048] tokens, 32/8 heads: every pool byte, and
     sampled output rows (first, last and random tokens of every prompt)."""
