@@ -93,6 +93,21 @@ def oracle_rows(w, k_ref, v_ref, rows):
     return orun.attend(w, k_ref, v_ref, rows=rows)
 
 
+@pytest.mark.parametrize("partition_size", [0, 16])
+def test_largest_batch(partition_size):
+    """4096 sequences, the most one call takes (the work plan every workgroup
+    keeps in LDS grows with the batch), short random contexts, whole pairs and
+    one-block slices."""
+    rng = np.random.default_rng(720 + partition_size)
+    lens = rng.integers(1, 41, size=4096)
+    nb = int(sum((int(x) + 15) // 16 for x in lens)) + 16
+    w = wl.decode_workload(f"largest_batch_p{partition_size}", 720 + partition_size, dtype=wl.BF16,
+                           num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                           num_blocks=nb, context_lens=[int(x) for x in lens],
+                           partition_size=partition_size)
+    _full_check(w)
+
+
 def test_context_one_reads_v0_exactly():
     for dtype in (wl.F32, wl.BF16):
         w = wl.decode_workload("ctx1", 31, dtype=dtype, num_q_heads=8, num_kv_heads=2,
