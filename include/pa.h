@@ -368,7 +368,7 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
  * already be in the pool: pa_write_kv first).  max_q_len (host) bounds every
  * q_len and sizes the launch; a longer q_len is truncated to it.
  *
- * Supported: PA_BF16 pools, head_dim 128, num_q_heads / num_kv_heads in
+ * Supported: PA_BF16 pools, head_dim 64 or 128, num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}.  QK^T and PV run on bf16 matrix cores with fp32
  * accumulation; the probabilities are rounded to bf16 for the PV product.
  */

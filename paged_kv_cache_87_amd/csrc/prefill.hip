@@ -1,6 +1,6 @@
-// Batched causal prefill for gfx950 on bf16 matrix cores: every new token of
-// every sequence attends to its paged history up to and including its own
-// position, all in one launch (JuliaPagedAttn README, "Features": batched
+// Batched causal prefill for gfx950 on bf16 matrix cores (head_dim 64 or 128):
+// every new token of every sequence attends to its paged history up to and
+// including its own position, all in one launch (JuliaPagedAttn README, "Features": batched
 // prefill, all prompt positions in a single kernel call; "Online Softmax").
 //
 // Work decomposition
@@ -50,12 +50,13 @@ namespace {
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kD = 128;               // head_dim handled here
 constexpr int kCols = 128;            // (head, token) columns per workgroup
 constexpr int kKeys = 32;             // keys per K/V tile (2 blocks)
 constexpr int kHalves = kKeys / 32;   // 32-key halves per tile = loader passes
-constexpr int kKStride = kD + 8;      // LDS row stride of K (bf16 elements): 68 dwords
-constexpr int kVStride = kD + 16;     // ... of V: 72 dwords, conflict-free transposing reads
+// LDS row strides of K and V (bf16 elements): at head_dim 128, 68 and 72 dwords,
+// the second conflict-free for the transposing reads
+template <int D> constexpr int kKStride = D + 8;
+template <int D> constexpr int kVStride = D + 16;
 constexpr float kPNegBig = -1.0e30f;
 constexpr float kPRescale = 8.f;
 
@@ -66,9 +67,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+template <int D>
 struct PrefillSmem {
-  uint16_t k[2][kKeys][kKStride];     // K tile, [key][d]
-  uint16_t v[2][kKeys][kVStride];     // V tile, [key][d]
+  uint16_t k[2][kKeys][kKStride<D>];  // K tile, [key][d]
+  uint16_t v[2][kKeys][kVStride<D>];  // V tile, [key][d]
 };
 
 // x of lane ^ 32 through the gfx950 lane-half swap (no LDS round trip)
@@ -83,11 +85,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
 }
 
-template <int R>
+template <int R, int kD>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+  static_assert(kD == 64 || kD == 128, "head_dim 64 or 128");
   constexpr int NREP = 1 << R;
   constexpr int TQ = kCols / NREP;    // tokens per tile
-  __shared__ PrefillSmem sm;
+  constexpr int kCPR = kD / 8;        // 16-byte chunks per K/V row
+  constexpr int kEPW = kCPR / 8;      // keys per lane and pass in the loader (2 or 1)
+  __shared__ PrefillSmem<kD> sm;
 
   const int tid = threadIdx.x;
   // ---- which tile: the dies take (sequence, KV head) pairs round-robin -------
@@ -189,14 +194,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const uint32_t row_bytes = a.geom.token_stride;     // next token row of one KV head
   const uint32_t block_bytes = a.geom.span;           // a block's rows (both layouts)
 
-  // ---- K/V tile loader: kKeys keys x 128 d, K and V as [key][d] rows --------
-  // thread -> (key pair 8 w + 2 (lane / 16) (+32 per further pass), d chunk
-  // dc = lane % 16): the keys of one wave and pass lie in one 16-token block,
+  // ---- K/V tile loader: kKeys keys x kD d, K and V as [key][d] rows ---------
+  // thread -> (keys 8 w + kEPW (lane / kCPR) + 0 .. kEPW - 1 (+32 per further
+  // pass), d chunk dc = lane % kCPR): wave w loads keys 8 w .. 8 w + 7 of a
+  // pass, so the keys of one wave and pass lie in one 16-token block,
   // so its block id is wave-uniform and the loads go through a buffer
   // descriptor; keys past the context read as zeros (offset past the
   // descriptor's size), so no pool row outside the context reaches the P.V
-  const int ld_key = 8 * wave + 2 * (lane >> 4);   // 0, 2, ..., 30
-  const int ld_dc = lane & 15;                      // 8-element chunk of d
+  const int ld_key = 8 * wave + kEPW * (lane / kCPR);   // first of the lane's keys
+  const int ld_dc = lane % kCPR;                         // 8-element chunk of d
   const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
     }
   };
-  uint4 kreg[kHalves][2], vreg[kHalves][2];  // [pass][key of the pair]
+  uint4 kreg[kHalves][kEPW], vreg[kHalves][kEPW];  // [pass][key of the lane's run]
   auto fetch = [&](int kt, const int (&ids)[kHalves]) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps) {
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
       const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < kEPW; ++e) {
         const int kpos = kt * kKeys + ld_key + 32 * ps + e;
         const uint32_t off = kpos < L ? ld_off + e * row_bytes : block_bytes;
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < kEPW; ++e) {
         const int key = ld_key + 32 * ps + e;
         *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 8]) = kreg[ps][e];
         *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 8]) = vreg[ps][e];
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int tr_row = 4 * half + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  f32x16 o[kD / 32];                  // O^T: 4 d-tiles of 32 x (32 columns)
+  f32x16 o[kD / 32];                  // O^T: kD / 32 d-tiles of 32 x (32 columns)
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
@@ -378,6 +384,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
+template <int D>
+hipError_t launch_heads(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_kernel(prefill_kernel<0, D>, grid, dim3(kPThreads), 0, stream, a);
+    case 2: return launch_kernel(prefill_kernel<1, D>, grid, dim3(kPThreads), 0, stream, a);
+    case 4: return launch_kernel(prefill_kernel<2, D>, grid, dim3(kPThreads), 0, stream, a);
+    case 8: return launch_kernel(prefill_kernel<3, D>, grid, dim3(kPThreads), 0, stream, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int n_rep = a.num_q_heads / a.num_kv_heads;
   const int tq = kCols / n_rep;
@@ -389,14 +406,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t per_die = (pairs + 7) / 8 * tiles;
   if (per_die <= 0) return hipSuccess;
   if (8 * per_die > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(8 * per_die));
-  switch (n_rep) {
-    case 1: return launch_kernel(prefill_kernel<0>, grid, dim3(kPThreads), 0, stream, a);
-    case 2: return launch_kernel(prefill_kernel<1>, grid, dim3(kPThreads), 0, stream, a);
-    case 4: return launch_kernel(prefill_kernel<2>, grid, dim3(kPThreads), 0, stream, a);
-    case 8: return launch_kernel(prefill_kernel<3>, grid, dim3(kPThreads), 0, stream, a);
-    default: return hipErrorInvalidValue;
-  }
+  const dim3 grid(static_cast<unsigned>(8 * per_die));
+  if (a.head_dim == 128) return launch_heads<128>(a, grid, stream);
+  if (a.head_dim == 64) return launch_heads<64>(a, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

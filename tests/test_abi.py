@@ -161,8 +161,8 @@ def test_prefill_checks(lib):
     f32 = pool(dtype=pa.PA_F32)
     assert lib.pa_prefill(ctypes.byref(f32), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
                           None) == pa.PA_ERR_UNSUPPORTED
-    d64 = pool(head_dim=64)
-    assert lib.pa_prefill(ctypes.byref(d64), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
+    d96 = pool(head_dim=96)
+    assert lib.pa_prefill(ctypes.byref(d96), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
                           None) == pa.PA_ERR_UNSUPPORTED
     p = pool()
     assert lib.pa_prefill(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE, 0, 10, 10, 8, 0.1,

@@ -48,6 +48,19 @@ def test_prefill_small_full_prompts(n_rep):
     _full(w)
 
 
+@pytest.mark.parametrize("num_q_heads,num_kv_heads", [(12, 12), (8, 2), (16, 2)])
+def test_prefill_head_dim_64(num_q_heads, num_kv_heads):
+    """head_dim 64 (the GPT-2 shape of the pages' model at 12/12 heads, and GQA
+    groups of 4 and 8): whole prompts across the tile edges, and prompts that
+    continue a history."""
+    w = wl.prefill_workload(f"prefill_d64_{num_q_heads}_{num_kv_heads}", 660 + num_q_heads,
+                            dtype=wl.BF16, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                            head_dim=64, block_size=16, num_blocks=512,
+                            context_lens=[1, 7, 31, 32, 33, 64, 119, 300, 503, 129],
+                            q_lens=[1, 7, 31, 32, 33, 64, 119, 300, 200, 1])
+    _full(w)
+
+
 @pytest.mark.parametrize("n_rep", [1, 4, 8])
 def test_prefill_chunked_continuation(n_rep):
     """q_len < context: the new tokens continue an existing history."""
