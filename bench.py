@@ -348,7 +348,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode path shards by sequence or KV head with no exchange; "
-              "this build runs on a single MI355X)", file=sys.stderr)
+              "this benchmark runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
