@@ -242,6 +242,8 @@ def pa_slot_mapping(pool: KVPool, seqs: SeqDesc, slot_mapping: torch.Tensor,
                     q_start_loc: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     lib = load_library()
     _validate_seqs(pool, seqs)
+    if q_start_loc is not None:
+        _check_q_start_loc(q_start_loc, seqs.block_tables.shape[0], slot_mapping.numel())
     qsl = 0 if q_start_loc is None else _dev(q_start_loc, "q_start_loc", torch.int32)
     cp, cs = pool.c(), seqs.c()
     st = lib.pa_slot_mapping(ctypes.byref(cp), ctypes.byref(cs), qsl or None,
@@ -297,6 +299,20 @@ def check_slots(slot_mapping, num_blocks: int, block_size: int = 16) -> None:
 def _validate_seqs(pool: KVPool, seqs: "SeqDesc") -> None:
     if validating():
         check_tables(seqs.block_tables, seqs.context_lens, pool.num_blocks, seqs.max_context_len)
+
+
+def _check_q_start_loc(q_start_loc: torch.Tensor, num_seqs: int, num_tokens: int) -> None:
+    """The kernels read q_start_loc[0 .. num_seqs]: its length is checked on
+    every call; with PA_VALIDATE=1 also that it is non-decreasing from 0 or
+    more to at most num_tokens."""
+    if tuple(q_start_loc.shape) != (num_seqs + 1,):
+        raise ValueError(f"q_start_loc must be [num_seqs + 1] = [{num_seqs + 1}], "
+                         f"got {tuple(q_start_loc.shape)}")
+    if validating():
+        loc = q_start_loc.cpu().numpy().astype(np.int64)
+        if loc[0] < 0 or loc[-1] > num_tokens or np.any(np.diff(loc) < 0):
+            raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
+                                      "q_start_loc is not non-decreasing within [0, num_tokens]")
 
 
 def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -384,6 +400,7 @@ def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
         raise ValueError("q's head_dim differs from the pool's")
     if tuple(out.shape) != (T, Hq, D):
         raise ValueError("out must have q's shape")
+    _check_q_start_loc(q_start_loc, seqs.block_tables.shape[0], T)
     cp, cs = pool.c(), seqs.c()
     st = lib.pa_prefill(ctypes.byref(cp), ctypes.byref(cs), _dev(q, "q", pool.dtype),
                         _dev(out, "out", pool.dtype), _dev(q_start_loc, "q_start_loc", torch.int32),

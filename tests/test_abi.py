@@ -219,3 +219,19 @@ def test_binding_rejects_host_tensors():
         p.c()
     with pytest.raises(ValueError):
         pa.KVPool(t, torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16))
+
+
+def test_binding_checks_q_start_loc_length(lib):
+    """q_start_loc must hold num_seqs + 1 offsets; the binding refuses another
+    length before anything reaches the library (no GPU needed)."""
+    import torch
+    from paged_kv_cache_87_amd import binding as bpa
+    k = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16)
+    kv = bpa.KVPool(k, torch.zeros_like(k), "token")
+    sd = bpa.SeqDesc(torch.zeros(3, 2, dtype=torch.int32), torch.ones(3, dtype=torch.int32), 32)
+    q = torch.zeros(5, 8, 64, dtype=torch.bfloat16)
+    for bad in (torch.zeros(3, dtype=torch.int32), torch.zeros(5, dtype=torch.int32)):
+        with pytest.raises(ValueError, match="q_start_loc"):
+            bpa.pa_prefill(kv, sd, q, torch.zeros_like(q), bad, 5, 0.125)
+        with pytest.raises(ValueError, match="q_start_loc"):
+            bpa.pa_slot_mapping(kv, sd, torch.zeros(5, dtype=torch.int64), bad)

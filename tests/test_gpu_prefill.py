@@ -216,3 +216,20 @@ def test_mixed_decode_and_prefill_batch():
         torch.cuda.synchronize()
         assert_close(out.float().cpu().numpy().astype(np.float64), out_ref[rows], w.dtype,
                      f"decode rows, partition {part}")
+
+
+def test_validate_mode_rejects_bad_q_start_loc(monkeypatch):
+    """With PA_VALIDATE=1, decreasing offsets or offsets past the token count
+    are reported before any launch."""
+    w = wl.prefill_workload("prefill_validate", 670, dtype=wl.BF16, num_q_heads=8, num_kv_heads=2,
+                            head_dim=128, block_size=16, num_blocks=64, context_lens=[20, 30])
+    announce(w.name)
+    g = _run(w)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    T = int(w.q_start_loc[-1])
+    for bad in ([0, 25, 20], [0, 20, T + 1]):
+        loc = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        with pytest.raises(pa.PagedAttentionError):
+            pa.pa_prefill(g.pool, g.seqs, g.q, g.out, loc, g.max_q_len, w.scale)
+    pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, g.max_q_len, w.scale)   # valid: runs
+    torch.cuda.synchronize()
