@@ -39,7 +39,9 @@ Conventions (readings where the pages are silent; each is pinned by a test):
   one written this step.  A context length of 0 gives an all-zero output.
 * Prefill query ``i`` of a sequence with ``q_len`` new tokens sits at
   position ``context_len - q_len + i`` and attends to positions
-  ``0 .. context_len - q_len + i`` (causal, diagonal included).
+  ``0 .. context_len - q_len + i`` (causal, diagonal included); a query
+  whose position is negative (more new tokens than the context holds) sees
+  no key and gives zeros.
 
 Arithmetic: stored values are upcast exactly to float64 and every sum,
 exponential and division is done in float64.  The softmax is the plain
@@ -231,54 +233,50 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype):
     return out
 
 
-def decode_one(q_row, k_cache, v_cache, block_table_row, context_len, scale, dtype,
-               q_head, num_q_heads):
-    """One output row of ``decode`` (sequence fixed by its table row and
-    context length), for sampled checks at sizes where the full oracle is
-    too slow."""
-    Hkv = k_cache.shape[2]
-    g = kv_head_of(q_head, num_q_heads, Hkv)
-    L = int(context_len)
-    keys = to_f64(gather_history(k_cache[:, :, g:g + 1], block_table_row, L), dtype)[:, 0]
-    vals = to_f64(gather_history(v_cache[:, :, g:g + 1], block_table_row, L), dtype)[:, 0]
-    return sdpa_two_pass(to_f64(q_row, dtype), keys, vals, scale)
-
-
-def prefill(q, k_cache, v_cache, block_tables, context_lens, q_start_loc, scale, dtype,
-            rows=None):
+def prefill(q, k_cache, v_cache, block_tables, context_lens, q_start_loc, scale, dtype):
     """Causal attention for every new token of every sequence (JuliaPagedAttn
     "Features": batched prefill, all prompt positions in one call).
 
     ``q`` is ``[T, Hq, D]`` (tokens of sequence ``s`` at ``q_start_loc[s] ..
     q_start_loc[s+1]-1``).  Query ``i`` of sequence ``s`` sits at position
-    ``p = context_lens[s] - q_len + i`` and attends to positions ``0..p``.
-    Returns float64 ``[T, Hq, D]``; with ``rows`` (a list of token indices)
-    only those rows are computed and the rest stay zero.
+    ``p = context_lens[s] - q_len + i`` and attends to positions ``0..p``
+    (causal, its own position included).  A query whose position is negative
+    (more new tokens than the context holds) sees no key and gives zeros.
+    Returns float64 ``[T, Hq, D]``.
+
+    Per sequence and query head, the scores of all its queries against all
+    its keys are one matrix product; keys after a query's position are left
+    out of that query's row; then each row takes the same two-pass softmax as
+    ``sdpa_two_pass`` (row maximum over the visible keys, exponentials and
+    their sum, the weighted sum of value rows).
     """
     T, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     _check_heads(Hq, Hkv)
     qf = to_f64(q, dtype)
     out = np.zeros((T, Hq, D), dtype=np.float64)
-    wanted = None if rows is None else set(int(r) for r in rows)
     positions = token_positions(context_lens, q_start_loc)
     q_start_loc = np.asarray(q_start_loc)
     for s in range(len(context_lens)):
         lo, hi = int(q_start_loc[s]), int(q_start_loc[s + 1])
-        if hi == lo or (wanted is not None and not any(lo <= r < hi for r in wanted)):
+        if hi == lo:
             continue
         L = int(context_lens[s])
         keys = to_f64(gather_history(k_cache, block_tables[s], L), dtype)
         vals = to_f64(gather_history(v_cache, block_tables[s], L), dtype)
-        for t in range(lo, hi):
-            if wanted is not None and t not in wanted:
-                continue
-            _, pos = positions[t]
-            n_visible = max(pos + 1, 0)
-            for h in range(Hq):
-                g = kv_head_of(h, Hq, Hkv)
-                out[t, h] = sdpa_two_pass(qf[t, h], keys[:n_visible, g, :],
-                                          vals[:n_visible, g, :], scale)
+        pos = np.array([positions[t][1] for t in range(lo, hi)], dtype=np.int64)
+        # key t is visible to a query at position p when t <= p
+        visible = np.arange(L)[None, :] <= pos[:, None]
+        rows = np.nonzero(visible.any(axis=1))[0]       # queries that see a key
+        if rows.size == 0:
+            continue
+        visible = visible[rows]
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            scores = scale * (qf[lo + rows, h] @ keys[:, g, :].T)
+            m = np.where(visible, scores, -np.inf).max(axis=1, keepdims=True)
+            p = np.exp(np.where(visible, scores - m, -np.inf))
+            out[lo + rows, h] = (p @ vals[:, g, :]) / p.sum(axis=1, keepdims=True)
     return out
 
 
@@ -342,6 +340,6 @@ def max_abs_err(gpu_f64: np.ndarray, ref_f64: np.ndarray) -> float:
 __all__ = [
     "F32", "BF16", "bf16_bits_to_f64", "to_f64", "token_positions", "slot_mapping",
     "write_kv_cache", "gather_history", "read_through_table", "sdpa_two_pass",
-    "kv_head_of", "decode", "decode_one", "prefill", "partition_stats", "lse_merge",
+    "kv_head_of", "decode", "prefill", "partition_stats", "lse_merge",
     "tolerance", "max_abs_err",
 ]

@@ -43,27 +43,19 @@ def write_step(w, k_cache, v_cache):
     return slots
 
 
-def attend(w, k_cache, v_cache, rows=None):
+def attend(w, k_cache, v_cache):
     """Attention output (float64) after the step's write."""
     if w.kind == "decode":
-        if rows is None:
-            return pa.decode(w.q, k_cache, v_cache, w.block_tables, w.context_lens,
-                             w.scale, w.dtype)
-        out = {}
-        for (s, h) in rows:
-            out[(s, h)] = pa.decode_one(w.q[s, h], k_cache, v_cache, w.block_tables[s],
-                                        w.context_lens[s], w.scale, w.dtype, h,
-                                        w.num_q_heads)
-        return out
+        return pa.decode(w.q, k_cache, v_cache, w.block_tables, w.context_lens, w.scale, w.dtype)
     return pa.prefill(w.q, k_cache, v_cache, w.block_tables, w.context_lens, w.q_start_loc,
-                      w.scale, w.dtype, rows=rows)
+                      w.scale, w.dtype)
 
 
-def run_step(w, rows=None):
+def run_step(w):
     """Pools, slots and attention output for one step of ``w``."""
     k_cache, v_cache = build_pools(w)
     slots = write_step(w, k_cache, v_cache)
-    out = attend(w, k_cache, v_cache, rows=rows)
+    out = attend(w, k_cache, v_cache)
     return k_cache, v_cache, slots, out
 
 

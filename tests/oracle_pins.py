@@ -130,6 +130,12 @@ def check_golden_attention(orc):
     qp[:, 0, :] = np.array(g["prefill_q"], dtype=np.float32)
     out = orc.prefill(qp, k_cache, v_cache, table, lens, np.array([0, 3]), 1.0, orc.F32)
     assert np.max(np.abs(out[:, 0, :] - np.array(g["prefill_expected_head0"]))) < tol, out
+    # four new tokens over the three-token context: the oldest has no position
+    qs = np.zeros((4, 2, 2), dtype=np.float32)
+    qs[:, 0, :] = np.array(g["short_prefill_q"], dtype=np.float32)
+    out = orc.prefill(qs, k_cache, v_cache, table, lens, np.array([0, 4]), 1.0, orc.F32)
+    assert np.all(np.isfinite(out)), out
+    assert np.max(np.abs(out[:, 0, :] - np.array(g["short_prefill_expected_head0"]))) < tol, out
     # context length 1 reads v0 exactly
     out = orc.decode(q, k_cache, v_cache, table, np.array([1]), 1.0, orc.F32)
     assert np.array_equal(out[0, 0], np.array(g["values"][0])), out
@@ -259,6 +265,46 @@ def check_brute_force_prefill(orc):
                 want = brute_force_attention(q[t, h], hk[s][:pos + 1, g].tolist(),
                                              hv[s][:pos + 1, g].tolist(), scale)
                 assert np.max(np.abs(out[t, h] - np.array(want))) < 1e-12, (s, i, h)
+
+
+def check_brute_force_prefill_short_context(orc):
+    """More new tokens than the context holds: a token whose position
+    (context length - q_len + i) is negative sees no key and gives zeros;
+    every other row is brute-force attention over positions 0..p.  An empty
+    context gives zeros for all its tokens.  GQA groups of 3, ragged tables."""
+    rng = _rng(22)
+    B, N, Hq, Hkv, D, scale = 4, 32, 6, 2, 3, 0.6
+    ctx = [5, 0, 9, 3]
+    qlen = [8, 2, 9, 1]           # longer than the context, empty context, whole, decode
+    tables = _random_tables(rng, [max(L, 1) for L in ctx], B, N)
+    hk = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in ctx]
+    hv = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in ctx]
+    k_cache, v_cache, la = _scatter_logical(orc, hk, hv, tables, B, N)
+    qsl = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32)
+    out = orc.prefill(q, k_cache, v_cache, tables, la, qsl, scale, orc.F32)
+    assert np.all(np.isfinite(out))
+    n_rep = Hq // Hkv
+    for s in range(len(ctx)):
+        for i in range(qlen[s]):
+            t = int(qsl[s]) + i
+            pos = ctx[s] - qlen[s] + i
+            for h in range(Hq):
+                g = h // n_rep
+                if pos < 0:
+                    assert np.array_equal(out[t, h], np.zeros(D)), (s, i, h)
+                    continue
+                want = brute_force_attention(q[t, h], hk[s][:pos + 1, g].tolist(),
+                                             hv[s][:pos + 1, g].tolist(), scale)
+                assert np.max(np.abs(out[t, h] - np.array(want))) < 1e-12, (s, i, h)
+    # scores in the thousands: finite, and the brute-force value
+    big = (q * 1000).astype(np.float32)
+    out = orc.prefill(big, k_cache, v_cache, tables, la, qsl, 1.0, orc.F32)
+    assert np.all(np.isfinite(out))
+    s, i, h = 2, 8, 5
+    t, g = int(qsl[s]) + i, h // n_rep
+    want = brute_force_attention(big[t, h], hk[s][:, g].tolist(), hv[s][:, g].tolist(), 1.0)
+    assert np.max(np.abs(out[t, h] - np.array(want))) < 1e-9
 
 
 # ---------------------------------------------------------------------------
@@ -452,6 +498,7 @@ def check_prefill_rows_equal_decode(orc):
 ALL_CHECKS = [
     check_golden_slots, check_golden_attention, check_bf16_constants, check_write_roundtrip,
     check_gather_equals_paged_read, check_brute_force_decode, check_brute_force_prefill,
+    check_brute_force_prefill_short_context,
     check_closed_forms, check_gqa_equals_repeated_mha, check_variable_lengths,
     check_partial_block_poison, check_cow_shared_equals_copied, check_partition_merge,
     check_prefill_rows_equal_decode,

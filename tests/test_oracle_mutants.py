@@ -37,8 +37,25 @@ MUTANTS = [
      "p = np.exp(scores)\n    return (p @ values) / p.sum()"),
     ("not_normalised", "return (p @ values) / p.sum()", "return (p @ values)"),
     ("transposed_operand", "return (p @ values) / p.sum()", "return (p @ keys) / p.sum()"),
-    ("causal_excludes_diagonal", "n_visible = max(pos + 1, 0)", "n_visible = max(pos, 0)"),
-    ("causal_one_extra", "n_visible = max(pos + 1, 0)", "n_visible = max(pos + 2, 0)"),
+    ("causal_excludes_diagonal", "visible = np.arange(L)[None, :] <= pos[:, None]",
+     "visible = np.arange(L)[None, :] < pos[:, None]"),
+    ("causal_one_extra", "visible = np.arange(L)[None, :] <= pos[:, None]",
+     "visible = np.arange(L)[None, :] <= pos[:, None] + 1"),
+    ("prefill_scale_dropped", "scores = scale * (qf[lo + rows, h] @ keys[:, g, :].T)",
+     "scores = (qf[lo + rows, h] @ keys[:, g, :].T)"),
+    ("prefill_no_max_subtraction", "np.where(visible, scores - m, -np.inf)",
+     "np.where(visible, scores, -np.inf)"),
+    ("prefill_max_over_masked_keys", "m = np.where(visible, scores, -np.inf).max(axis=1, keepdims=True)",
+     "m = scores.max(axis=1, keepdims=True)"),
+    ("prefill_not_normalised", "(p @ vals[:, g, :]) / p.sum(axis=1, keepdims=True)",
+     "(p @ vals[:, g, :])"),
+    ("prefill_transposed_operand", "(p @ vals[:, g, :]) / p.sum(axis=1, keepdims=True)",
+     "(p @ keys[:, g, :]) / p.sum(axis=1, keepdims=True)"),
+    ("prefill_rows_not_shifted", "out[lo + rows, h] =", "out[lo + np.arange(rows.size), h] ="),
+    ("prefill_keeps_rows_without_keys", "rows = np.nonzero(visible.any(axis=1))[0]",
+     "rows = np.arange(visible.shape[0])"),
+    ("prefill_query_from_wrong_head", "scores = scale * (qf[lo + rows, h] @ keys[:, g, :].T)",
+     "scores = scale * (qf[lo + rows, g] @ keys[:, g, :].T)"),
     ("merge_weight_sign", "w = np.asarray(l, dtype=np.float64) * np.exp(m - M)",
      "w = np.asarray(l, dtype=np.float64) * np.exp(M - m)"),
     ("merge_drops_l", "w = np.asarray(l, dtype=np.float64) * np.exp(m - M)", "w = np.exp(m - M)"),
