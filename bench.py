@@ -10,8 +10,9 @@ resident in HBM.
 
 Printed: one JSON line with whole-step throughput (K/V bytes read per
 second), the decode call's roofline (K/V bytes / decode kernel time against
-8 TB/s, timed with events over the timed region), the CPU oracle timed on a
-bounded sample of the same workload, and secondary measurements of the
+8 TB/s, timed with events over the timed region), the split the decode ran
+(workgroups, slice length, pieces per pair), the CPU oracle timed on one
+whole step of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16), of the
 long-context shared-prefix decode, of the copy-on-write block copy and of
 the block swap between the device pool and a pinned host pool.
@@ -50,8 +51,8 @@ def parse():
     p.add_argument("--layout", default="token",
                    help="pool layout of the headline decode (token, head, unified_token, "
                         "unified_head, layers_token, layers_head)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="wall-time budget of the CPU oracle sample")
+    p.add_argument("--cpu-runs", type=int, default=3,
+                   help="timed runs of the CPU oracle step (the median is reported)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--no-secondary", action="store_true",
                    help="skip the prefill and long-context measurements")
@@ -88,32 +89,44 @@ def measured_traffic(workload_name: str, partition_size: int):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle as it stands on the host: pools built and the step's write
-    done untimed, then decode of whole sequences, in order (wrapping around),
-    until the time budget is used up."""
+def cpu_baseline(w, runs: int = 3):
+    """The oracle as it stands, on the host cores: one whole step of the
+    headline workload -- the K/V write of the 64 new tokens, then the decode
+    of every sequence -- with the sequences spread over a thread pool (one
+    sequence per task, longest first, numpy's own BLAS held to one thread per
+    worker).  The pre-step history is written into the pools untimed; the
+    step is timed `runs` times and the median taken."""
+    import concurrent.futures as cf
+    import statistics
+
     from oracle import run as orun
     import oracle.paged_attention as orc
+
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl absent or unreadable
-        blas_threads = 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # threadpoolctl absent: BLAS keeps its own thread count
+        threadpool_limits = None
     k_cache, v_cache = orun.build_pools(w)
-    orun.write_step(w, k_cache, v_cache)
-    done, kv_bytes, tokens = 0, 0, 0
-    elt = 2 if w.dtype == "bf16" else 4
-    t0 = time.perf_counter()
-    while True:
-        s = done % w.num_seqs
-        orc.decode(w.q[s:s + 1], k_cache, v_cache, w.block_tables[s:s + 1],
-                   w.context_lens[s:s + 1], w.scale, w.dtype)
-        done += 1
-        tokens += int(w.context_lens[s])
-        kv_bytes += 2 * w.num_kv_heads * w.head_dim * elt * int(w.context_lens[s])
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    order = sorted(range(w.num_seqs), key=lambda s: -int(w.context_lens[s]))
+
+    def one(s):
+        return orc.decode(w.q[s:s + 1], k_cache, v_cache, w.block_tables[s:s + 1],
+                          w.context_lens[s:s + 1], w.scale, w.dtype)
+
+    times = []
+    limit = threadpool_limits(1) if threadpool_limits is not None else None
+    try:
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                orun.write_step(w, k_cache, v_cache)
+                list(ex.map(one, order))
+                times.append(time.perf_counter() - t0)
+    finally:
+        if limit is not None:
+            limit.unregister()
+    step_s = statistics.median(times)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -123,15 +136,18 @@ def cpu_baseline(w, budget_s: float):
                     break
     except OSError:
         pass
+    kv_bytes = w.kv_bytes_read()
     return {
-        "value": kv_bytes / dt / 1e9,
+        "value": kv_bytes / step_s / 1e9,
         "unit": "GB/s",
-        "cores": int(blas_threads),
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{done} sequence decodes of this workload in order ({done / w.num_seqs:.2f} passes, "
-                  f"{tokens} context tokens, {kv_bytes / 1e9:.3f} GB of K/V) in {dt:.1f} s, numpy "
-                  f"float64; host CPU {model!r}, {len(os.sched_getaffinity(0))} cores visible",
-        "seconds": dt,
+        "sample": f"the whole step of this workload (write of {w.num_seqs} new tokens, decode of "
+                  f"{w.num_seqs} sequences, {kv_bytes / 1e9:.3f} GB of K/V), median of {runs} runs "
+                  f"({', '.join(f'{t:.2f}' for t in times)} s), numpy float64 over a pool of "
+                  f"{workers} threads, BLAS at 1 thread each; host CPU {model!r}, "
+                  f"{len(os.sched_getaffinity(0))} cores visible",
+        "us_per_step": step_s * 1e6,
     }
 
 
@@ -256,6 +272,8 @@ def secondary(torch, np, stream, K, W, partition_size):
     w = wl.long_context_cow(pool_fill="zero")
     g = runner.GpuStep(w)
     g.write_history()
+    from paged_kv_cache_87_amd import binding as _b
+    lc_split = _b.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, w.partition_size)
     step_ms, dec_ms = timed(torch, stream, K, W, g.append, g.attend)
     dec = float(np.mean(dec_ms))
     logical = w.kv_bytes_read()
@@ -263,7 +281,7 @@ def secondary(torch, np, stream, K, W, partition_size):
     unique = logical - (w.num_seqs - 1) * prefix * 2 * w.num_kv_heads * w.head_dim * 2
     out["long_context_cow"] = {
         "config": {"batch": w.num_seqs, "context": int(w.context_lens[0]), "shared_prefix": prefix,
-                   "partition_size": w.partition_size},
+                   "partition_size": w.partition_size, "decode_split": lc_split},
         "us_per_step": step_ms * 1e3, "decode_us": dec * 1e3,
         "logical_kv_GBps": logical / (dec * 1e-3) / 1e9,
         "unique_kv_GBps": unique / (dec * 1e-3) / 1e9,
@@ -326,7 +344,15 @@ def secondary(torch, np, stream, K, W, partition_size):
     out["hbm_copy_ceiling"] = {"bytes_moved": 2 << 30,
                                "GBps": (2 << 30) / (float(np.mean(cp_ms)) * 1e-3) / 1e9}
     out["hbm_copy_ceiling"]["frac_hbm_peak"] = out["hbm_copy_ceiling"]["GBps"] / HBM_PEAK_GBPS
-    del a, b
+    del b
+    # and a plain read stream: torch's sum over the same 1 GiB (as float32)
+    a32 = a.view(torch.float32)
+    a32.fill_(1.0)
+    _, rd_ms = timed(torch, stream, K, W, lambda: None, lambda: a32.sum())
+    out["hbm_read_ceiling"] = {"bytes_read": 1 << 30,
+                               "GBps": (1 << 30) / (float(np.mean(rd_ms)) * 1e-3) / 1e9}
+    out["hbm_read_ceiling"]["frac_hbm_peak"] = out["hbm_read_ceiling"]["GBps"] / HBM_PEAK_GBPS
+    del a, a32
     return out
 
 
@@ -384,6 +410,7 @@ def main():
     kv_bytes = w.kv_bytes_read()
     stream = torch.cuda.current_stream()
 
+    split = binding.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, args.partition_size)
     K = args.steps
     step_ms, decode_ms = timed(torch, stream, K, args.warmup, g.append, g.attend)
     dec_avg_ms = float(np.mean(decode_ms))
@@ -394,7 +421,7 @@ def main():
 
     sec = None if args.no_secondary else secondary(torch, np, stream, max(10, K // 5), 30,
                                                        args.partition_size)
-    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
+    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_runs)
 
     traffic = measured_traffic(w.name, args.partition_size) if args.layout == "token" else None
     rec = {
@@ -424,6 +451,7 @@ def main():
             "sum_context_tokens": sum_ctx,
             "kv_bytes_per_step": kv_bytes,
             "partition_size": args.partition_size,
+            "decode_split": split,
             "pool_layout": args.layout,
         },
         "decode_us": {"mean": dec_avg_ms * 1e3, "p10": float(np.percentile(decode_ms, 10)) * 1e3,

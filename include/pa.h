@@ -356,17 +356,49 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_split_info -- how pa_decode would split this batch (host only,
+ * nothing launched; needs the device the decode would run on to be current).
+ *
+ * host_context_lens (host, int32 [num_seqs]) is a host copy of
+ * seqs->context_lens; the other arguments are those of pa_decode (q, out and
+ * the workspace are not needed).  Fills *info: the workgroups of the launch;
+ * slice_blocks, the work each workgroup takes in blocks (each segment of a
+ * (sequence, KV head) pair priced as a fixed number of extra blocks), 0 when
+ * the context is not split; and how many pieces the non-empty pairs are cut
+ * into (1 each when not split).  partition_size is a lower bound of the
+ * slice, not the slice itself: the slice is the larger of partition_size / 16
+ * blocks and the batch's work divided by the workgroups.
+ */
+typedef struct pa_decode_split {
+  int32_t workgroups;
+  int32_t slice_blocks;
+  int32_t pairs;        /* (sequence, KV head) pairs with a non-empty context */
+  int32_t max_pieces;   /* most pieces of one pair */
+  float mean_pieces;    /* mean pieces per pair */
+} pa_decode_split;
+
+pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                               const int32_t* host_context_lens, int32_t num_q_heads,
+                               int32_t partition_size, pa_decode_split* info);
+
+/*
  * pa_prefill -- causal attention of every new token of every sequence over
  * its paged history, in one call (JuliaPagedAttn "Features": batched
  * prefill, all prompt positions processed in a single kernel call).
  *
  * q (device, [total_q_tokens, num_q_heads, head_dim]) and out (same shape)
  * are in the pool's dtype, 16-byte aligned.  q_start_loc (device, int32
- * [num_seqs+1]) lists each sequence's tokens as in pa_slot_mapping; token
- * q_start_loc[s]+i sits at position p = context_lens[s] - q_len + i and
- * attends to positions 0 .. p of its sequence (the K/V of the new tokens must
- * already be in the pool: pa_write_kv first).  max_q_len (host) bounds every
- * q_len and sizes the launch; a longer q_len is truncated to it.
+ * [num_seqs+1]) lists each sequence's tokens as in pa_slot_mapping (its
+ * entries are clamped to [0, total_q_tokens], so no row outside q and out is
+ * touched); token q_start_loc[s]+i of a sequence with q_len new tokens sits
+ * at position p = context_lens[s] - q_len + i and attends to positions
+ * 0 .. p of its sequence (the K/V of the new tokens must already be in the
+ * pool: pa_write_kv first).  A token whose position is negative (q_len
+ * above the context length) sees no key and its row of out is zero.
+ * max_q_len (host) bounds every q_len and sizes the launch: of a sequence
+ * with more new tokens, only the newest max_q_len are computed, each at its
+ * own position, and the rows of the older ones are not written.  Keys whose
+ * table entry is not a block of the pool get no weight (as in pa_decode).
  *
  * Supported: PA_BF16 pools, head_dim 64 or 128, num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}.  QK^T and PV run on bf16 matrix cores with fp32

@@ -40,6 +40,7 @@ EXPORTED = (
     "pa_allocator_destroy", "pa_allocator_num_free", "pa_allocator_refcount",
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
     "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks", "pa_append_kv",
+    "pa_decode_split_info",
 )
 
 
@@ -64,6 +65,16 @@ class PaSeqDesc(ctypes.Structure):
         ("num_seqs", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_context_len", ctypes.c_int32),
+    ]
+
+
+class PaDecodeSplit(ctypes.Structure):
+    _fields_ = [
+        ("workgroups", ctypes.c_int32),
+        ("slice_blocks", ctypes.c_int32),
+        ("pairs", ctypes.c_int32),
+        ("max_pieces", ctypes.c_int32),
+        ("mean_pieces", ctypes.c_float),
     ]
 
 
@@ -106,6 +117,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_copy_blocks": (i32, [pool_p, vp, vp, i32, vp]),
         "pa_swap_blocks": (i32, [pool_p, pool_p, vp, vp, i32, i32, vp]),
         "pa_append_kv": (i32, [pool_p, seq_p, vp, vp, vp, vp]),
+        "pa_decode_split_info": (i32, [pool_p, seq_p, vp, i32, i32, ctypes.POINTER(PaDecodeSplit)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -301,10 +313,14 @@ def _validate_seqs(pool: KVPool, seqs: "SeqDesc") -> None:
         check_tables(seqs.block_tables, seqs.context_lens, pool.num_blocks, seqs.max_context_len)
 
 
-def _check_q_start_loc(q_start_loc: torch.Tensor, num_seqs: int, num_tokens: int) -> None:
+def _check_q_start_loc(q_start_loc: torch.Tensor, num_seqs: int, num_tokens: int,
+                       context_lens: Optional[torch.Tensor] = None,
+                       max_q_len: Optional[int] = None) -> None:
     """The kernels read q_start_loc[0 .. num_seqs]: its length is checked on
-    every call; with PA_VALIDATE=1 also that it is non-decreasing from 0 or
-    more to at most num_tokens."""
+    every call.  With PA_VALIDATE=1 also that it is non-decreasing from 0 or
+    more to at most num_tokens, and (prefill) that no sequence has more new
+    tokens than max_q_len (the older ones would not be computed) or than its
+    context length (the oldest would have no position and get zeros)."""
     if tuple(q_start_loc.shape) != (num_seqs + 1,):
         raise ValueError(f"q_start_loc must be [num_seqs + 1] = [{num_seqs + 1}], "
                          f"got {tuple(q_start_loc.shape)}")
@@ -313,6 +329,20 @@ def _check_q_start_loc(q_start_loc: torch.Tensor, num_seqs: int, num_tokens: int
         if loc[0] < 0 or loc[-1] > num_tokens or np.any(np.diff(loc) < 0):
             raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
                                       "q_start_loc is not non-decreasing within [0, num_tokens]")
+        q_lens = np.diff(loc)
+        if max_q_len is not None and q_lens.size and int(q_lens.max()) > max_q_len:
+            s = int(q_lens.argmax())
+            raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
+                                      f"sequence {s} has {int(q_lens[s])} new tokens, more than "
+                                      f"max_q_len {max_q_len}")
+        if context_lens is not None:
+            cl = context_lens.cpu().numpy().astype(np.int64)
+            over = np.nonzero(q_lens > cl)[0]
+            if over.size:
+                s = int(over[0])
+                raise PagedAttentionError("PA_VALIDATE", PA_ERR_INVALID_ARG,
+                                          f"sequence {s} has {int(q_lens[s])} new tokens, more "
+                                          f"than its context length {int(cl[s])}")
 
 
 def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -359,6 +389,23 @@ def pa_decode_workspace_bytes(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
                                                         num_q_heads, partition_size))
 
 
+def pa_decode_split_info(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
+                         partition_size: int) -> dict:
+    """How pa_decode splits this batch: workgroups, slice length in blocks
+    (0 = not split) and pieces per (sequence, KV head) pair.  Reads a host
+    copy of the context lengths."""
+    lens = np.ascontiguousarray(seqs.context_lens.cpu().numpy(), dtype=np.int32)
+    info = PaDecodeSplit()
+    cp, cs = pool.c(), seqs.c()
+    st = load_library().pa_decode_split_info(ctypes.byref(cp), ctypes.byref(cs),
+                                             lens.ctypes.data, int(num_q_heads),
+                                             int(partition_size), ctypes.byref(info))
+    _check("pa_decode_split_info", st)
+    return {"workgroups": info.workgroups, "slice_blocks": info.slice_blocks,
+            "pairs": info.pairs, "max_pieces": info.max_pieces,
+            "mean_pieces": float(info.mean_pieces)}
+
+
 def decode_workspace(pool: KVPool, seqs: SeqDesc, num_q_heads: int, partition_size: int,
                      device="cuda") -> Optional[torch.Tensor]:
     """A zeroed workspace for pa_decode (None when none is needed).  Zeroing
@@ -400,7 +447,8 @@ def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
         raise ValueError("q's head_dim differs from the pool's")
     if tuple(out.shape) != (T, Hq, D):
         raise ValueError("out must have q's shape")
-    _check_q_start_loc(q_start_loc, seqs.block_tables.shape[0], T)
+    _check_q_start_loc(q_start_loc, seqs.block_tables.shape[0], T, seqs.context_lens,
+                       int(max_q_len))
     cp, cs = pool.c(), seqs.c()
     st = lib.pa_prefill(ctypes.byref(cp), ctypes.byref(cs), _dev(q, "q", pool.dtype),
                         _dev(out, "out", pool.dtype), _dev(q_start_loc, "q_start_loc", torch.int32),
@@ -528,7 +576,7 @@ def pa_version() -> int:
 __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
-    "decode_workspace", "pa_decode", "pa_prefill", "BlockAllocator", "pa_copy_blocks",
+    "decode_workspace", "pa_decode", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit", "BlockAllocator", "pa_copy_blocks",
     "host_pool_c", "pa_swap_blocks", "paged_attention", "pa_append_kv", "check_tables", "check_slots",
     "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
     "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",

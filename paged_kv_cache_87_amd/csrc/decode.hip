@@ -174,8 +174,10 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // Partition results travel between workgroups that may sit on different
-// dies: device-scope atomic stores and loads, which go past the dies'
-// private caches.
+// dies: device-scope (agent) atomic stores and loads, which on gfx950 are
+// issued at the device-coherent level (sc1: written through, and read past,
+// a die's own L2).  Their order is set by the pair's arrival counter (see
+// the arrivals at the end of the kernel).
 __device__ __forceinline__ void store_shared(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -560,12 +562,13 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     float p[4];
 #pragma unroll
     for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
 
     if constexpr (sizeof(T) == 2) {
       // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
       // with one v_dot2_f32_bf16 per (head, element): the value rows of the
-      // pair are interleaved with v_perm, the weights packed to bf16.
+      // pair are interleaved with v_perm, the weights packed to bf16.  The
+      // running sum adds the same rounded weights (slot 0 is the lane's own
+      // head), so the normalised output is a convex combination of the V rows.
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -580,6 +583,8 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
           const f32x2 two = {pa[j], pb[j]};
           pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
         }
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[0]),
+                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), l, false);
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           // element 2w: low halves of token a and b; element 2w+1: high halves
@@ -597,6 +602,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
         }
       }
     } else {
+      l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu) {
         float pj[N];
@@ -769,10 +775,18 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   }
 
   // ---- arrivals of this slice's pieces ------------------------------------------
-  // The pieces' stores bypass the dies' private caches; once every wave has
-  // waited for its stores they are visible device-wide, before the count
-  // moves.  The last arrival of a pair merges its pieces and leaves the
-  // counter at zero for the next call.
+  // Publication: every wave waits until its piece stores (device-coherent
+  // atomic stores) are complete, then the workgroup barrier, then thread 0
+  // counts the pieces with an agent-scope add; the add therefore reaches
+  // memory after every piece store of the workgroup.  Acquisition: the
+  // workgroup whose add completes a pair runs an agent-scope acquire fence
+  // before the barrier that releases its threads to the merge, whose loads
+  // are device-coherent atomic loads.  The add itself is relaxed: an
+  // agent-scope release would add an L2 write-back (buffer_wbl2) per
+  // workgroup, which publishes plain stores this protocol does not use and
+  // cost 15 us a call on the 64-sequence random-length batch.  The last
+  // arrival of a pair merges its pieces and leaves the counter at zero for
+  // the next call.
   if (pa_s >= 0 || pb_s >= 0) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -790,6 +804,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       if (pb_s >= 0)
         last_b = __hip_atomic_fetch_add(a.counters + pb_s * Hkv + pb_g, 1, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT) == pieces(pb_s, pb_g) - 1;
+      if (last_a | last_b) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       sm_last[0] = last_a;
       sm_last[1] = last_b;
     }
@@ -814,7 +829,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
 // The persistent grid: what the device holds at once, but no more
 // workgroups than there are slices (split) or pairs (whole pairs).
 template <typename T, int D, int R>
-hipError_t run_typed(const DecodeArgs& a, hipStream_t stream) {
+hipError_t grid_typed(const DecodeArgs& a, int* grid) {
   const size_t lds = plan_lds_bytes(a.num_seqs);
   const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R>);
   int resident = 0;
@@ -824,34 +839,53 @@ hipError_t run_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t work = a.min_slice_blocks > 0
                            ? static_cast<int64_t>(a.max_slices)
                            : static_cast<int64_t>(a.num_kv_heads) * a.num_seqs;
-  const int grid = static_cast<int>(resident < work ? resident : (work > 0 ? work : 1));
-  return launch_kernel(decode_kernel<T, D, R>, dim3(grid), dim3(kThreads), lds, stream, a);
+  *grid = static_cast<int>(resident < work ? resident : (work > 0 ? work : 1));
+  return hipSuccess;
+}
+
+template <typename T, int D, int R>
+hipError_t run_typed(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
+  int grid = 0;
+  const hipError_t e = grid_typed<T, D, R>(a, &grid);
+  if (e != hipSuccess) return e;
+  if (grid_only != nullptr) {
+    *grid_only = grid;
+    return hipSuccess;
+  }
+  constexpr int kThreads = 64 * decode_waves<T, D, R>();
+  return launch_kernel(decode_kernel<T, D, R>, dim3(grid), dim3(kThreads),
+                       plan_lds_bytes(a.num_seqs), stream, a);
 }
 
 template <typename T, int D>
-hipError_t run_heads(const DecodeArgs& a, hipStream_t stream) {
+hipError_t run_heads(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return run_typed<T, D, 0>(a, stream);
-    case 2: return run_typed<T, D, 1>(a, stream);
-    case 4: return run_typed<T, D, 2>(a, stream);
-    case 8: return run_typed<T, D, 3>(a, stream);
+    case 1: return run_typed<T, D, 0>(a, stream, grid_only);
+    case 2: return run_typed<T, D, 1>(a, stream, grid_only);
+    case 4: return run_typed<T, D, 2>(a, stream, grid_only);
+    case 8: return run_typed<T, D, 3>(a, stream, grid_only);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t run(const DecodeArgs& a, hipStream_t stream) {
+// Launch the decode, or with grid_only set only report the grid it would use.
+hipError_t run(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   if (a.dtype == 1) {
-    if (a.head_dim == 128) return run_heads<uint16_t, 128>(a, stream);
-    if (a.head_dim == 64) return run_heads<uint16_t, 64>(a, stream);
+    if (a.head_dim == 128) return run_heads<uint16_t, 128>(a, stream, grid_only);
+    if (a.head_dim == 64) return run_heads<uint16_t, 64>(a, stream, grid_only);
   } else {
-    if (a.head_dim == 128) return run_heads<float, 128>(a, stream);
-    if (a.head_dim == 64) return run_heads<float, 64>(a, stream);
+    if (a.head_dim == 128) return run_heads<float, 128>(a, stream, grid_only);
+    if (a.head_dim == 64) return run_heads<float, 64>(a, stream, grid_only);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) { return run(a, stream); }
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return run(a, stream, nullptr);
+}
+
+hipError_t decode_grid(const DecodeArgs& a, int* grid) { return run(a, nullptr, grid); }
 
 }  // namespace pa

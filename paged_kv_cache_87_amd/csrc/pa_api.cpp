@@ -365,10 +365,16 @@ size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs
       .workspace_bytes;
 }
 
-pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q, void* out,
-                    int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode request shared by pa_decode and pa_decode_split_info,
+// and its kernel arguments (workspace pointers left null).  With io, q and
+// out are checked too.
+pa_status prepare_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
+                         void* out, int32_t num_q_heads, float scale, int32_t partition_size,
+                         bool io, pa::DecodeArgs* a, pa::DecodePlan* plan) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if ((st = check_seqs(seqs)) != PA_OK) return st;
@@ -377,60 +383,128 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
     return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a multiple of block_size %d",
                 partition_size, pool->block_size);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (seqs->num_seqs == 0) return PA_OK;
-  if (q == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "q or out is null");
-  if (!aligned16(q) || !aligned16(out))
-    return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  const pa::DecodePlan plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq,
-                                              seqs->max_context_len, pool->num_kv_heads,
-                                              num_q_heads, pool->head_dim, partition_size);
-  if (plan.max_blocks >= (int64_t(1) << 31))
+  if (io && seqs->num_seqs > 0) {
+    if (q == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "q or out is null");
+    if (!aligned16(q) || !aligned16(out))
+      return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  }
+  *plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, seqs->max_context_len,
+                          pool->num_kv_heads, num_q_heads, pool->head_dim, partition_size);
+  if (plan->max_blocks >= (int64_t(1) << 31))
     return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * num_seqs * context blocks = %lld (below 2^31)",
-                static_cast<long long>(plan.max_blocks));
+                static_cast<long long>(plan->max_blocks));
   if (seqs->num_seqs > pa::kMaxDecodeSeqs)
     return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most %d)", seqs->num_seqs,
                 pa::kMaxDecodeSeqs);
-  float* part_o = nullptr;
-  float* part_ml = nullptr;
-  int32_t* counters = nullptr;
+  if (plan->workspace_bytes > 0 &&
+      static_cast<int64_t>(seqs->num_seqs) * pool->num_kv_heads > pa::kCounterSlots)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads = %lld (at most %d when split)",
+                static_cast<long long>(seqs->num_seqs) * pool->num_kv_heads, pa::kCounterSlots);
+  *a = pa::DecodeArgs{};
+  a->q = q;
+  a->out = out;
+  a->k_cache = pool->k_cache;
+  a->v_cache = pool->v_cache;
+  a->block_tables = seqs->block_tables;
+  a->context_lens = seqs->context_lens;
+  a->num_seqs = seqs->num_seqs;
+  a->num_blocks = pool->num_blocks;
+  a->num_kv_heads = pool->num_kv_heads;
+  a->num_q_heads = num_q_heads;
+  a->head_dim = pool->head_dim;
+  a->dtype = pool->dtype;
+  a->max_blocks_per_seq = seqs->max_blocks_per_seq;
+  a->context_cap = plan->context_cap;
+  a->min_slice_blocks = plan->min_slice_blocks;
+  a->max_slices = plan->max_slices;
+  a->seg_cost = plan->min_slice_blocks > 0 ? pa::kSegCost : 0;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  a->geom = geom_of(pool);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q, void* out,
+                    int32_t num_q_heads, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  pa::DecodeArgs a;
+  pa::DecodePlan plan;
+  const pa_status st = prepare_decode(pool, seqs, q, out, num_q_heads, scale, partition_size,
+                                      true, &a, &plan);
+  if (st != PA_OK) return st;
+  if (seqs->num_seqs == 0) return PA_OK;
   if (plan.workspace_bytes > 0) {
-    if (static_cast<int64_t>(seqs->num_seqs) * pool->num_kv_heads > pa::kCounterSlots)
-      return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads = %lld (at most %d when split)",
-                  static_cast<long long>(seqs->num_seqs) * pool->num_kv_heads,
-                  pa::kCounterSlots);
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
                   plan.workspace_bytes, workspace == nullptr ? size_t(0) : workspace_bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    counters = static_cast<int32_t*>(workspace);
-    part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_offset);
-    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
+    a.counters = static_cast<int32_t*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_offset);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
   }
-  pa::DecodeArgs a{};
-  a.q = q;
-  a.out = out;
-  a.k_cache = pool->k_cache;
-  a.v_cache = pool->v_cache;
-  a.block_tables = seqs->block_tables;
-  a.context_lens = seqs->context_lens;
-  a.part_o = part_o;
-  a.part_ml = part_ml;
-  a.counters = counters;
-  a.num_seqs = seqs->num_seqs;
-  a.num_blocks = pool->num_blocks;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.num_q_heads = num_q_heads;
-  a.head_dim = pool->head_dim;
-  a.dtype = pool->dtype;
-  a.max_blocks_per_seq = seqs->max_blocks_per_seq;
-  a.context_cap = plan.context_cap;
-  a.min_slice_blocks = plan.min_slice_blocks;
-  a.max_slices = plan.max_slices;
-  a.seg_cost = plan.min_slice_blocks > 0 ? pa::kSegCost : 0;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.geom = geom_of(pool);
   return hip_status(pa::launch_decode(a, stream), "decode launch");
+}
+
+pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
+                               const int32_t* host_context_lens, int32_t num_q_heads,
+                               int32_t partition_size, pa_decode_split* info) {
+  clear_error();
+  if (info == nullptr) return fail(PA_ERR_INVALID_ARG, "info is null");
+  pa::DecodeArgs a;
+  pa::DecodePlan plan;
+  const pa_status st = prepare_decode(pool, seqs, nullptr, nullptr, num_q_heads, 1.f,
+                                      partition_size, false, &a, &plan);
+  if (st != PA_OK) return st;
+  if (seqs->num_seqs > 0 && host_context_lens == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "host_context_lens is null");
+  *info = pa_decode_split{};
+  if (seqs->num_seqs == 0) return PA_OK;
+  int grid = 0;
+  const pa_status hs = hip_status(pa::decode_grid(a, &grid), "decode grid query");
+  if (hs != PA_OK) return hs;
+  info->workgroups = grid;
+  // the kernel's plan, from the host copy of the lengths: pair (s, g) owns
+  // nb_s blocks priced nb_s + seg_cost, laid end to end; split, slice i
+  // covers work [i Q, (i + 1) Q)
+  const int H = pool->num_kv_heads;
+  const int C = a.seg_cost;
+  int64_t B = 0;
+  for (int s = 0; s < seqs->num_seqs; ++s) {
+    int L = host_context_lens[s];
+    L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
+    if (L > 0) B += static_cast<int64_t>(H) * ((L + pa::kBlockSize - 1) / pa::kBlockSize + C);
+  }
+  int64_t Q = 0;
+  if (a.min_slice_blocks > 0) {
+    Q = (B + grid - 1) / grid;
+    if (Q < a.min_slice_blocks) Q = a.min_slice_blocks;
+  }
+  info->slice_blocks = static_cast<int32_t>(Q);
+  int64_t pairs = 0, pieces = 0, pre = 0;
+  int32_t most = 0;
+  for (int s = 0; s < seqs->num_seqs; ++s) {
+    int L = host_context_lens[s];
+    L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
+    if (L == 0) continue;
+    const int64_t nb = (L + pa::kBlockSize - 1) / pa::kBlockSize;
+    for (int g = 0; g < H; ++g) {
+      const int64_t A = H * pre + g * (nb + C) + C;   // work position of the pair's block 0
+      const int64_t n = Q > 0 ? (A + nb - 1) / Q - A / Q + 1 : 1;
+      ++pairs;
+      pieces += n;
+      if (n > most) most = static_cast<int32_t>(n);
+    }
+    pre += nb + C;
+  }
+  info->pairs = static_cast<int32_t>(pairs);
+  info->max_pieces = most;
+  info->mean_pieces = pairs > 0 ? static_cast<float>(static_cast<double>(pieces) / pairs) : 0.f;
+  return PA_OK;
 }
 
 pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q, void* out,

@@ -123,6 +123,8 @@ struct DecodeArgs {
   PoolGeom geom;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Workgroups launch_decode(a) uses on the current device (nothing launched).
+hipError_t decode_grid(const DecodeArgs& a, int* grid);
 
 struct PrefillArgs {
   const void* q;

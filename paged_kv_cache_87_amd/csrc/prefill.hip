@@ -67,11 +67,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// 16-byte aligned, so that the tile rows are read and written with 16-byte
+// LDS instructions
 template <int D>
-struct PrefillSmem {
+struct alignas(16) PrefillSmem {
   uint16_t k[2][kKeys][kKStride<D>];  // K tile, [key][d]
   uint16_t v[2][kKeys][kVStride<D>];  // V tile, [key][d]
+  int bad[2][2 * kHalves];            // per 16-key block of a tile: its table entry is not a block
 };
+
+// The q / out rows of sequence s: [q0, q0 + q_len), q_start_loc clamped to
+// [0, total_q_tokens] so that no row outside the buffers is touched.
+__device__ __forceinline__ void seq_rows(const PrefillArgs& a, int s, int& q0, int& q_len) {
+  int lo = a.q_start_loc[s];
+  int hi = a.q_start_loc[s + 1];
+  lo = min(max(lo, 0), a.total_q_tokens);
+  hi = min(max(hi, lo), a.total_q_tokens);
+  q0 = lo;
+  q_len = hi - lo;
+}
 
 // x of lane ^ 32 through the gfx950 lane-half swap (no LDS round trip)
 __device__ __forceinline__ float xor32(float x) {
@@ -118,11 +132,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       int nt = 0;
       if (c0 + tid < mine) {
         const int ss = (die + 8 * (c0 + tid)) / a.num_kv_heads;
-        int ql = a.q_start_loc[ss + 1] - a.q_start_loc[ss];
-        int LL = a.context_lens[ss];
-        LL = LL < 0 ? 0 : (LL > a.context_cap ? a.context_cap : LL);
-        ql = ql < 0 ? 0 : (ql > a.max_q_len ? a.max_q_len : ql);
-        nt = (min(ql, LL) + TQ - 1) / TQ;
+        int q0, ql;
+        seq_rows(a, ss, q0, ql);
+        nt = (min(ql, a.max_q_len) + TQ - 1) / TQ;
       }
       // inclusive scan of the chunk's tile counts (Hillis-Steele in LDS)
       sm_scan[tid] = nt;
@@ -153,23 +165,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int half = lane >> 5;         // lane half: rows 4*half.. of each 8-row group
   const int col = lane & 31;          // this lane's column inside the wave
 
-  const int qs0 = a.q_start_loc[s];
-  int q_len = a.q_start_loc[s + 1] - qs0;
+  // The sequence's q_len new tokens sit at positions L - q_len .. L - 1.  The
+  // newest n_q = min(q_len, max_q_len) of them are computed, each at its own
+  // position (older rows are not written); a token whose position is
+  // negative sees no key and gets a zero row.
+  int qs0, q_len;
+  seq_rows(a, s, qs0, q_len);
   int L = a.context_lens[s];
   L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
-  q_len = q_len < 0 ? 0 : (q_len > a.max_q_len ? a.max_q_len : q_len);
-  if (q_len > L) q_len = L;  // queries without a position in the context are skipped
-  const int n_tiles = (q_len + TQ - 1) / TQ;
+  const int n_q = min(q_len, a.max_q_len);
+  const int row0 = qs0 + q_len - n_q;  // q / out row of computed token 0
+  const int n_tiles = (n_q + TQ - 1) / TQ;
   const int tile = n_tiles - 1 - sm_pick[2];      // heaviest tiles (most keys) first
   if (tile < 0) return;
   const int t0 = tile * TQ;
-  const int first_pos = L - q_len;    // position of new token 0
+  const int first_pos = L - n_q;      // position of computed token 0 (may be negative)
 
   // ---- this lane's column: (head, token) ----------------------------------
   const int c = wave * 32 + col;
   const int head = c / TQ;
   const int tok = t0 + c % TQ;
-  const bool col_valid = tok < q_len;
+  const bool col_valid = tok < n_q;
   const int qpos = first_pos + tok;   // the column's query position
   const int qh = g * NREP + head;
 
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   bf16x8 qf[kD / 16];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<int64_t>(qs0 + (col_valid ? tok : 0)) * a.num_q_heads + qh) * kD;
+                           (static_cast<int64_t>(row0 + (col_valid ? tok : 0)) * a.num_q_heads + qh) * kD;
 #pragma unroll
     for (int kk = 0; kk < kD / 16; ++kk) {
       uint4 x = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * half);
@@ -187,9 +203,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   }
 
   // last key any column of the tile needs
-  const int last_tok = min(t0 + TQ, q_len) - 1;
+  const int last_tok = min(t0 + TQ, n_q) - 1;
   const int key_end = first_pos + last_tok + 1;       // keys [0, key_end)
-  const int n_kt = (key_end + kKeys - 1) / kKeys;
+  const int n_kt = key_end > 0 ? (key_end + kKeys - 1) / kKeys : 0;
   const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
   const uint32_t row_bytes = a.geom.token_stride;     // next token row of one KV head
   const uint32_t block_bytes = a.geom.span;           // a block's rows (both layouts)
@@ -200,7 +216,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // pass, so the keys of one wave and pass lie in one 16-token block,
   // so its block id is wave-uniform and the loads go through a buffer
   // descriptor; keys past the context read as zeros (offset past the
-  // descriptor's size), so no pool row outside the context reaches the P.V
+  // descriptor's size), so no pool row outside the context reaches the P.V.
+  // A table entry that is not a block of the pool loads zeros too, and the
+  // first wave of each 16-key block records it (`bad`) so that its keys get
+  // no weight, as the decode skips such blocks
   const int ld_key = 8 * wave + kEPW * (lane / kCPR);   // first of the lane's keys
   const int ld_dc = lane % kCPR;                         // 8-element chunk of d
   const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
@@ -214,11 +233,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
   };
   uint4 kreg[kHalves][kEPW], vreg[kHalves][kEPW];  // [pass][key of the lane's run]
+  int kbad[kHalves];                                // the pass's block is not in the pool
   auto fetch = [&](int kt, const int (&ids)[kHalves]) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps) {
       const int phys = uniform(ids[ps]);
       const bool ok = phys >= 0 && phys < a.num_blocks;
+      kbad[ps] = ok ? 0 : 1;
       const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
       const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
       const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
@@ -236,13 +257,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int ps = 0; ps < kHalves; ++ps)
+    for (int ps = 0; ps < kHalves; ++ps) {
 #pragma unroll
       for (int e = 0; e < kEPW; ++e) {
         const int key = ld_key + 32 * ps + e;
         *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 8]) = kreg[ps][e];
         *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 8]) = vreg[ps][e];
       }
+      // waves 0 and 2 load the first keys of the tile's two blocks
+      if ((wave & 1) == 0 && lane == 0) sm.bad[buf][(wave >> 1) + 2 * ps] = kbad[ps];
+    }
   };
   // transposing-read source address of this lane: key row 4 * half + (lane % 16) / 4,
   // d column 16 * (lane / 16 mod 2) + 4 * (lane mod 4) (plus the step's offsets)
@@ -311,6 +335,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > lim) st[t][r] = -INFINITY;
       }
+      // keys of a block whose table entry is not in the pool get no weight
+      // (rows r < 8 are the half's first 16 keys, r >= 8 its second 16)
+      const int bad0 = sm.bad[buf][2 * t], bad1 = sm.bad[buf][2 * t + 1];
+      if (bad0 | bad1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (r < 8 ? bad0 : bad1) st[t][r] = -INFINITY;
+      }
       float tmax = st[t][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, st[t][r]);
@@ -370,7 +402,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   if (!col_valid) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(a.out) +
-                   (static_cast<int64_t>(qs0 + tok) * a.num_q_heads + qh) * kD;
+                   (static_cast<int64_t>(row0 + tok) * a.num_q_heads + qh) * kD;
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll

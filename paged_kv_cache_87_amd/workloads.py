@@ -247,7 +247,8 @@ def prefill_workload(name, seed, *, dtype, num_q_heads, num_kv_heads, head_dim,
         width = max(nblk) if nblk else 1
     tables = _tables(rng, nblk, num_blocks, width)
     hist_start = np.zeros(S, dtype=np.int32)
-    hist_end = (context_lens - q_lens).astype(np.int32)
+    # more new tokens than the context holds: nothing was written before
+    hist_end = np.maximum(context_lens - q_lens, 0).astype(np.int32)
     n_hist = int(hist_end.astype(np.int64).sum())
     T = int(q_lens.astype(np.int64).sum())
     Hkv, D = num_kv_heads, head_dim

@@ -31,13 +31,20 @@ def assert_pools_equal(gpu_step, k_ref, v_ref):
     assert vg.tobytes() == v_ref.tobytes(), "V pool differs from the oracle's"
 
 
+# (case, dtype, max abs error, tolerance) of every comparison with the oracle
+# in this session, printed at the end of the run by tests/conftest.py
+ERRORS = []
+
+
 def assert_close(gpu_f64, ref_f64, dtype, what=""):
     tol = orc.tolerance(dtype)
     assert np.all(np.isfinite(gpu_f64)), f"{what}: non-finite output"
     err = orc.max_abs_err(gpu_f64, ref_f64)
+    ERRORS.append((what, dtype, err, tol))
+    print(f"[gpu-case] {what}: max abs error {err:.3e} (tolerance {tol:.0e})", flush=True)
     assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.0e}"
     return err
 
 
-def oracle_step(w, rows=None):
-    return orun.run_step(w, rows=rows)
+def oracle_step(w):
+    return orun.run_step(w)

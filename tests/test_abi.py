@@ -235,3 +235,17 @@ def test_binding_checks_q_start_loc_length(lib):
             bpa.pa_prefill(kv, sd, q, torch.zeros_like(q), bad, 5, 0.125)
         with pytest.raises(ValueError, match="q_start_loc"):
             bpa.pa_slot_mapping(kv, sd, torch.zeros(5, dtype=torch.int64), bad)
+
+
+def test_split_info_rejects_bad_arguments(lib):
+    info = pa.PaDecodeSplit()
+    lens = (ctypes.c_int32 * 4)(10, 20, 30, 40)
+    assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), lens, 8, 0,
+                                    None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), None, 8, 0,
+                                    ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_split_info(ctypes.byref(pool(block_size=32)), ctypes.byref(seqs()), lens,
+                                    8, 0, ctypes.byref(info)) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), lens, 8, 24,
+                                    ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_last_error() != b""

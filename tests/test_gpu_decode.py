@@ -64,33 +64,31 @@ def test_llama_gqa_decode_full_size():
     _full_check(wl.llama_gqa_decode())
 
 
-def test_long_context_cow_sampled():
-    """Batch 16 at context 32768 sharing a 4096-token prefix; partition 512.
-    Every pool byte is compared; outputs on sampled (sequence, head) rows."""
-    w = wl.long_context_cow()
-    announce(w.name)
-    g = runner.run_workload(w)
-    k_ref, v_ref = orun_build_and_write(w)
-    assert_pools_equal(g, k_ref, v_ref)
-    rng = np.random.Generator(np.random.PCG64(7))
-    rows = [(int(s), int(h)) for s, h in zip(rng.integers(0, 16, 12), rng.integers(0, 32, 12))]
-    rows += [(0, 0), (15, 31)]
-    ref = oracle_rows(w, k_ref, v_ref, rows)
-    out = g.out_f64()
-    got = np.stack([out[s, h] for (s, h) in rows])
-    assert_close(got, np.stack([ref[r] for r in rows]), w.dtype, w.name)
+def test_long_context_cow_full_size():
+    """Batch 16 at context 32768 sharing a 4096-token prefix (256 shared
+    blocks), partition 512: every pool byte and every output row against the
+    oracle."""
+    _full_check(wl.long_context_cow())
 
 
-def orun_build_and_write(w):
-    from oracle import run as orun
-    k_ref, v_ref = orun.build_pools(w)
-    orun.write_step(w, k_ref, v_ref)
-    return k_ref, v_ref
-
-
-def oracle_rows(w, k_ref, v_ref, rows):
-    from oracle import run as orun
-    return orun.attend(w, k_ref, v_ref, rows=rows)
+@pytest.mark.parametrize("num_q_heads,num_kv_heads", [(32, 8), (8, 1)])
+def test_one_long_pair_in_many_pieces(num_q_heads, num_kv_heads):
+    """One sequence of 32768 tokens with the smallest partition (one block):
+    the slices are ~65 blocks at 32/8 heads (about 32 pieces per (sequence,
+    KV head) pair) and ~9 blocks at 8/1 heads (about 230 pieces of one pair),
+    all merged by log-sum-exp in the kernel."""
+    w = wl.decode_workload(f"long_pair_h{num_q_heads}_{num_kv_heads}", 730 + num_kv_heads,
+                           dtype=wl.BF16, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                           head_dim=128, block_size=16, num_blocks=2100, context_lens=[32768],
+                           partition_size=16)
+    from paged_kv_cache_87_amd import binding as pa
+    g = runner.GpuStep(w)
+    split = pa.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, 16)
+    announce(f"{w.name} split {split}")
+    assert split["pairs"] == num_kv_heads
+    assert split["max_pieces"] >= (30 if num_kv_heads == 8 else 200), split
+    del g
+    _full_check(w)
 
 
 @pytest.mark.parametrize("partition_size", [0, 16])
@@ -320,6 +318,24 @@ def test_append_equals_slot_mapping_then_write(dtype, layout):
     assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
     assert_pools_equal(g, k_ref, v_ref)
     assert_close(g.out_f64(), out_ref, w.dtype, w.name)
+
+
+def test_append_full_size_llama_gqa():
+    """The bench's write path at its own size: pa_append_kv of the 64 new
+    tokens (8 KV heads x 128, bf16) into the 40000-block pool, then the
+    split decode; slots and every pool byte bit for bit, every output row
+    within tolerance."""
+    w = wl.llama_gqa_decode(partition_size=1024)
+    announce(w.name + " append")
+    g = runner.GpuStep(w)
+    g.write_history()
+    g.append()
+    g.attend()
+    torch.cuda.synchronize()
+    k_ref, v_ref, slots_ref, out_ref = oracle_step(w)
+    assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
+    assert_pools_equal(g, k_ref, v_ref)
+    assert_close(g.out_f64(), out_ref, w.dtype, w.name + " append")
 
 
 def test_unrelated_hip_error_is_not_blamed_on_a_launch():

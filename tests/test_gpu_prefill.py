@@ -117,24 +117,10 @@ def test_prefill_many_pairs_per_die(num_seqs, num_kv_heads, hi):
     _full(w)
 
 
-def test_prefill_batched_full_size_sampled():
-    """16 prompts of U[256, 2048] tokens, 32/8 heads: every pool byte, and
-    sampled output rows (first, last and random tokens of every prompt)."""
-    w = wl.batched_prefill()
-    announce(w.name)
-    g = _run(w)
-    k_ref, v_ref = orun.build_pools(w)
-    slots_ref = orun.write_step(w, k_ref, v_ref)
-    assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
-    assert_pools_equal(g, k_ref, v_ref)
-    rng = np.random.Generator(np.random.PCG64(11))
-    rows = []
-    for s in range(w.num_seqs):
-        lo, hi = int(w.q_start_loc[s]), int(w.q_start_loc[s + 1])
-        rows += [lo, hi - 1] + [int(x) for x in rng.integers(lo, hi, 3)]
-    ref = orun.attend(w, k_ref, v_ref, rows=rows)
-    out = g.out_f64()
-    assert_close(out[rows], ref[rows], w.dtype, w.name)
+def test_prefill_batched_full_size():
+    """16 prompts of U[256, 2048] tokens, 32/8 heads: every pool byte and
+    every output row against the oracle."""
+    _full(wl.batched_prefill())
 
 
 def test_prefill_row_equals_decode():
@@ -232,4 +218,119 @@ def test_validate_mode_rejects_bad_q_start_loc(monkeypatch):
         with pytest.raises(pa.PagedAttentionError):
             pa.pa_prefill(g.pool, g.seqs, g.q, g.out, loc, g.max_q_len, w.scale)
     pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, g.max_q_len, w.scale)   # valid: runs
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n_rep", [1, 4])
+def test_prefill_more_new_tokens_than_context(n_rep):
+    """q_len above the context length: token i of a sequence keeps its
+    position context_len - q_len + i, so the oldest q_len - context_len
+    tokens have no position, see no key and get zero rows (their slots are
+    -1 and nothing is written for them); the other rows match the oracle.
+    Cases across the 32-token query tile edge, and an empty context."""
+    lens = [5, 40, 0, 33, 100]
+    q_lens = [9, 70, 3, 33, 140]
+    w = wl.prefill_workload(f"prefill_short_ctx_r{n_rep}", 680 + n_rep, dtype=wl.BF16,
+                            num_q_heads=2 * n_rep, num_kv_heads=2, head_dim=128, block_size=16,
+                            num_blocks=256, context_lens=lens, q_lens=q_lens)
+    announce(w.name)
+    g = _run(w)
+    k_ref, v_ref, slots_ref, out_ref = orun.run_step(w)
+    assert np.array_equal(g.slots.cpu().numpy(), slots_ref), "slot mapping differs"
+    assert_pools_equal(g, k_ref, v_ref)
+    out = g.out_f64()
+    for s in range(len(lens)):
+        lo = int(w.q_start_loc[s])
+        dead = max(q_lens[s] - lens[s], 0)
+        assert np.array_equal(out[lo:lo + dead], np.zeros_like(out[lo:lo + dead])), s
+    assert_close(out, out_ref, w.dtype, w.name)
+
+
+def test_prefill_tokens_past_max_q_len():
+    """A sequence with more new tokens than max_q_len: its newest max_q_len
+    tokens are computed, each at its own position; the older rows are not
+    written (they keep the NaN the output starts with).  Every other row
+    matches the oracle."""
+    lens = [300, 90, 64]
+    q_lens = [300, 90, 10]
+    w = wl.prefill_workload("prefill_past_max_q_len", 690, dtype=wl.BF16, num_q_heads=16,
+                            num_kv_heads=4, head_dim=128, block_size=16, num_blocks=256,
+                            context_lens=lens, q_lens=q_lens)
+    announce(w.name)
+    g = runner.GpuStep(w)
+    g.write_history()
+    g.slot_mapping()
+    g.write()
+    max_q = 70
+    pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, max_q, w.scale)
+    torch.cuda.synchronize()
+    _, _, _, out_ref = orun.run_step(w)
+    out = g.out_f64()
+    done = np.zeros(out.shape[0], dtype=bool)
+    for s in range(len(lens)):
+        lo, hi = int(w.q_start_loc[s]), int(w.q_start_loc[s + 1])
+        done[max(lo, hi - max_q):hi] = True
+    assert np.all(np.isnan(out[~done])), "rows older than max_q_len were written"
+    assert_close(out[done], out_ref[done], w.dtype, w.name)
+
+
+def test_prefill_out_of_pool_table_entry():
+    """A table entry inside the context that is not a block of the pool: its
+    16 keys get no weight (as in pa_decode), and every other key does.  The
+    expected rows are the oracle's two-pass softmax over the positions that
+    remain; each row also equals pa_decode at context i + 1 over the same
+    table."""
+    L, bad_block = 150, 3
+    w = wl.prefill_workload("prefill_bad_entry", 695, dtype=wl.BF16, num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, block_size=16, num_blocks=64,
+                            context_lens=[L])
+    announce(w.name)
+    g = _run(w)
+    k_ref, v_ref, _, _ = orun.run_step(w)
+    bad = g.block_tables.clone()
+    bad[0, bad_block] = w.num_blocks + 7
+    seqs = pa.SeqDesc(bad, g.context_lens, L)
+    out = torch.full_like(g.q, float("nan"))
+    pa.pa_prefill(g.pool, seqs, g.q, out, g.q_start_loc, L, w.scale)
+    torch.cuda.synchronize()
+    import oracle.paged_attention as orc
+    keys = orc.to_f64(orc.gather_history(k_ref, w.block_tables[0], L), w.dtype)
+    vals = orc.to_f64(orc.gather_history(v_ref, w.block_tables[0], L), w.dtype)
+    qf = orc.to_f64(w.q, w.dtype)
+    keep = np.array([p // 16 != bad_block for p in range(L)])
+    ref = np.zeros(qf.shape)
+    for i in range(L):
+        vis = keep[:i + 1]
+        for h in range(w.num_q_heads):
+            g_ = h // (w.num_q_heads // w.num_kv_heads)
+            ref[i, h] = orc.sdpa_two_pass(qf[i, h], keys[:i + 1][vis, g_], vals[:i + 1][vis, g_],
+                                          w.scale)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert_close(got, ref, w.dtype, w.name)
+    rows = [0, 47, 48, 63, 64, 65, 149]
+    lens = torch.tensor([r + 1 for r in rows], dtype=torch.int32, device="cuda")
+    dseqs = pa.SeqDesc(bad.expand(len(rows), -1).contiguous(), lens, L)
+    q = g.q[rows].contiguous()
+    dout = torch.full_like(q, float("nan"))
+    pa.pa_decode(g.pool, dseqs, q, dout, w.scale, 0, None)
+    torch.cuda.synchronize()
+    assert_close(dout.float().cpu().numpy().astype(np.float64), ref[rows], w.dtype,
+                 w.name + " decode rows")
+
+
+def test_validate_mode_rejects_long_q_len(monkeypatch):
+    """With PA_VALIDATE=1, a sequence with more new tokens than max_q_len or
+    than its context length is reported before any launch."""
+    w = wl.prefill_workload("prefill_validate_qlen", 671, dtype=wl.BF16, num_q_heads=8,
+                            num_kv_heads=2, head_dim=128, block_size=16, num_blocks=64,
+                            context_lens=[20, 30], q_lens=[20, 30])
+    announce(w.name)
+    g = _run(w)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    with pytest.raises(pa.PagedAttentionError):       # q_len 30 > max_q_len 25
+        pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, 25, w.scale)
+    short = pa.SeqDesc(g.block_tables, torch.tensor([20, 29], dtype=torch.int32, device="cuda"), 30)
+    with pytest.raises(pa.PagedAttentionError):       # q_len 30 > context 29
+        pa.pa_prefill(g.pool, short, g.q, g.out, g.q_start_loc, 30, w.scale)
+    pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, 30, w.scale)   # valid: runs
     torch.cuda.synchronize()
