@@ -356,6 +356,33 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode without a caller workspace, for callers
+ * that cannot allocate device memory around the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments and results are those of pa_decode with workspace NULL: the
+ * split decode's arrival counters and partial results live instead in a
+ * device array of the library's own, pa_decode_noalloc_max_bytes() bytes
+ * (16.5 MiB: the largest workspace pa_decode_workspace_bytes can ask for),
+ * which every GPU the library runs on holds until the process ends.  The
+ * call allocates and frees nothing.  Its first call on a device looks up
+ * that device's copy of the array and clears the counters with a small
+ * kernel on `stream`; every call leaves them zero again.
+ *
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  A request whose split would need more than the array holds
+ * returns PA_ERR_UNSUPPORTED and enqueues nothing; other errors are those
+ * of pa_decode.
+ */
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
+                            void* out, int32_t num_q_heads, float scale, int32_t partition_size,
+                            hipStream_t stream);
+
+/* Bytes of the array pa_decode_noalloc uses per GPU (host only). */
+size_t pa_decode_noalloc_max_bytes(void);
+
+/*
  * pa_decode_split_info -- how pa_decode would split this batch (host only,
  * nothing launched; needs the device the decode would run on to be current).
  *

@@ -40,7 +40,7 @@ EXPORTED = (
     "pa_allocator_destroy", "pa_allocator_num_free", "pa_allocator_refcount",
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
     "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks", "pa_append_kv",
-    "pa_decode_split_info",
+    "pa_decode_split_info", "pa_decode_noalloc", "pa_decode_noalloc_max_bytes",
 )
 
 
@@ -118,6 +118,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_swap_blocks": (i32, [pool_p, pool_p, vp, vp, i32, i32, vp]),
         "pa_append_kv": (i32, [pool_p, seq_p, vp, vp, vp, vp]),
         "pa_decode_split_info": (i32, [pool_p, seq_p, vp, i32, i32, ctypes.POINTER(PaDecodeSplit)]),
+        "pa_decode_noalloc": (i32, [pool_p, seq_p, vp, vp, i32, f32, i32, vp]),
+        "pa_decode_noalloc_max_bytes": (sz, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -437,6 +439,26 @@ def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, s
     return out
 
 
+def pa_decode_noalloc(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
+                      scale: float, partition_size: int = 0, stream=None) -> torch.Tensor:
+    """pa_decode without a workspace: the split's counters and partial
+    results live in the library's own per-GPU device array (calls on one GPU
+    must not overlap)."""
+    lib = load_library()
+    _validate_seqs(pool, seqs)
+    S, Hq, D = q.shape
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must have q's shape")
+    if D != _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)[3]:
+        raise ValueError("q's head_dim differs from the pool's")
+    cp, cs = pool.c(), seqs.c()
+    st = lib.pa_decode_noalloc(ctypes.byref(cp), ctypes.byref(cs), _dev(q, "q", pool.dtype),
+                               _dev(out, "out", pool.dtype), Hq, float(scale),
+                               int(partition_size), _stream(stream))
+    _check("pa_decode_noalloc", st)
+    return out
+
+
 def pa_prefill(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
                q_start_loc: torch.Tensor, max_q_len: int, scale: float,
                stream=None) -> torch.Tensor:
@@ -576,7 +598,8 @@ def pa_version() -> int:
 __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
-    "decode_workspace", "pa_decode", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit", "BlockAllocator", "pa_copy_blocks",
+    "decode_workspace", "pa_decode", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit",
+    "pa_decode_noalloc", "BlockAllocator", "pa_copy_blocks",
     "host_pool_c", "pa_swap_blocks", "paged_attention", "pa_append_kv", "check_tables", "check_slots",
     "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
     "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",

@@ -450,6 +450,95 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
   return hip_status(pa::launch_decode(a, stream), "decode launch");
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: the split decode's counters and partial results in a
+// device array of the library's own, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Largest split decode workspace: the counter header, then partial outputs
+// and (max, sum) pairs of 2 * kMaxSlices slots of 8 query heads x head_dim
+// 128 (see plan_decode).
+constexpr size_t kScratchBytes = pa::kCounterHeaderBytes +
+                                 size_t(2) * pa::kMaxSlices * 8 * 128 * sizeof(float) +
+                                 size_t(2) * pa::kMaxSlices * 8 * 2 * sizeof(float);
+
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code this name is only a handle for hipGetSymbolAddress, never a
+// device address.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+struct ZeroArgs {
+  uint32_t* p;
+  uint32_t n;     // words
+};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(ZeroArgs z) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < z.n; i += gridDim.x * 256u) z.p[i] = 0u;
+}
+
+// The current device's copy of `scratch`, looked up once per device; the
+// first lookup also zeroes its counter header on `stream` (a fill kernel,
+// so that a caller capturing the stream into a graph records no memset).
+pa_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "hipGetSymbolAddress(scratch)");
+    const ZeroArgs z{static_cast<uint32_t*>(ptr),
+                     static_cast<uint32_t>(pa::kCounterHeaderBytes / sizeof(uint32_t))};
+    e = pa::launch_kernel(zero_words_kernel, dim3(64), dim3(256), 0, stream, z);
+    if (e != hipSuccess) return hip_status(e, "scratch counter clear");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+pa_status pa_decode_noalloc(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
+                            void* out, int32_t num_q_heads, float scale, int32_t partition_size,
+                            hipStream_t stream) {
+  clear_error();
+  pa::DecodeArgs a;
+  pa::DecodePlan plan;
+  const pa_status st = prepare_decode(pool, seqs, q, out, num_q_heads, scale, partition_size,
+                                      true, &a, &plan);
+  if (st != PA_OK) return st;
+  if (seqs->num_seqs == 0) return PA_OK;
+  if (plan.workspace_bytes > kScratchBytes)
+    return fail(PA_ERR_UNSUPPORTED,
+                "this split needs %zu bytes of scratch; pa_decode_noalloc holds %zu",
+                plan.workspace_bytes, kScratchBytes);
+  if (plan.workspace_bytes > 0) {
+    void* ptr = nullptr;
+    const pa_status ss = scratch_for_current_device(stream, &ptr);
+    if (ss != PA_OK) return ss;
+    a.counters = static_cast<int32_t*>(ptr);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(ptr) + plan.part_o_offset);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ptr) + plan.part_ml_offset);
+  }
+  return hip_status(pa::launch_decode(a, stream), "decode launch");
+}
+
 pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
                                const int32_t* host_context_lens, int32_t num_q_heads,
                                int32_t partition_size, pa_decode_split* info) {

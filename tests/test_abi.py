@@ -249,3 +249,16 @@ def test_split_info_rejects_bad_arguments(lib):
     assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), lens, 8, 24,
                                     ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_last_error() != b""
+
+
+def test_noalloc_rejects_bad_arguments(lib):
+    def call(p, s, q=FAKE, out=FAKE, hq=8, scale=0.1, part=0):
+        return lib.pa_decode_noalloc(ctypes.byref(p), ctypes.byref(s), q, out, hq, scale, part,
+                                     None)
+    assert call(pool(block_size=32), seqs()) == pa.PA_ERR_UNSUPPORTED
+    assert call(pool(), seqs(), hq=5) == pa.PA_ERR_INVALID_ARG
+    assert call(pool(), seqs(), part=24) == pa.PA_ERR_INVALID_ARG
+    assert call(pool(), seqs(), q=0) == pa.PA_ERR_INVALID_ARG
+    assert call(pool(), seqs(num_seqs=5000)) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_last_error() != b""
+    assert lib.pa_decode_noalloc_max_bytes() == (256 + 16 * 1024 + 256) * 1024
