@@ -427,9 +427,11 @@ pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
  * own position, and the rows of the older ones are not written.  Keys whose
  * table entry is not a block of the pool get no weight (as in pa_decode).
  *
- * Supported: PA_BF16 pools, head_dim 64 or 128, num_q_heads / num_kv_heads in
- * {1, 2, 4, 8}.  QK^T and PV run on bf16 matrix cores with fp32
- * accumulation; the probabilities are rounded to bf16 for the PV product.
+ * Supported: PA_BF16 and PA_F32 pools, head_dim 64 or 128, num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}.  QK^T and PV run on the matrix cores with
+ * fp32 accumulation: bf16 pools on bf16 matrix instructions (the
+ * probabilities rounded to bf16 for the PV product), fp32 pools on fp32 ones
+ * (nothing rounded below fp32).
  */
 pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
                      void* out, const int32_t* q_start_loc, int32_t total_q_tokens,

@@ -604,8 +604,6 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
   if (st != PA_OK) return st;
   if ((st = check_seqs(seqs)) != PA_OK) return st;
   if ((st = check_heads(pool, num_q_heads)) != PA_OK) return st;
-  if (pool->dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 pools");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
   if (total_q_tokens < 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID_ARG, "total_q_tokens %d / max_q_len %d < 0", total_q_tokens,
@@ -632,6 +630,7 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
   a.context_cap = context_cap(seqs);
   a.max_q_len = max_q_len;
   a.total_q_tokens = total_q_tokens;
+  a.dtype = pool->dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.geom = geom_of(pool);
   return hip_status(pa::launch_prefill(a, stream), "prefill launch");

@@ -143,6 +143,7 @@ struct PrefillArgs {
   int32_t context_cap;
   int32_t max_q_len;
   int32_t total_q_tokens;
+  int32_t dtype;           // 0 = f32, 1 = bf16
   float scale_log2;
   PoolGeom geom;
 };

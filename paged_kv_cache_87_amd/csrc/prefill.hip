@@ -99,6 +99,57 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
 }
 
+// ---- which tile: the dies take (sequence, KV head) pairs round-robin -------
+// Workgroups are handed to the eight dies (XCDs) round-robin by linear id,
+// so linear id i runs on die i mod 8.  Die x works through the pairs x,
+// x + 8, x + 16, ... one after the other, each pair's tiles heaviest first:
+// every tile of a pair then runs on the die whose L2 already holds the
+// pair's K/V, and with eight KV heads each die gets one head of every
+// sequence, the same work.  The grid is an upper bound; surplus workgroups
+// find no tile (sm_pick[0] < 0) and leave.  Otherwise sm_pick holds the
+// sequence, the KV head and the tile's place among the pair's tiles
+// (0 = the heaviest).  TQ is the tokens per tile.
+__device__ __forceinline__ void pick_tile(const PrefillArgs& a, int TQ, int* sm_scan,
+                                          int* sm_pick) {
+  const int tid = threadIdx.x;
+  const int lin = blockIdx.x;
+  const int die = lin & 7;
+  const int want = lin >> 3;                    // index in this die's queue of tiles
+  const int npairs = a.num_seqs * a.num_kv_heads;
+  const int mine = (npairs - die + 7) / 8;      // pairs die, die + 8, ...
+  if (tid == 0) sm_pick[0] = -1;
+  __syncthreads();
+  int base = 0;                                 // tiles of the die's earlier chunks
+  for (int c0 = 0; c0 < mine; c0 += kPThreads) {
+    int nt = 0;
+    if (c0 + tid < mine) {
+      const int ss = (die + 8 * (c0 + tid)) / a.num_kv_heads;
+      int q0, ql;
+      seq_rows(a, ss, q0, ql);
+      nt = (min(ql, a.max_q_len) + TQ - 1) / TQ;
+    }
+    // inclusive scan of the chunk's tile counts (Hillis-Steele in LDS)
+    sm_scan[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < kPThreads; off <<= 1) {
+      const int y = tid >= off ? sm_scan[tid - off] : 0;
+      __syncthreads();
+      sm_scan[tid] += y;
+      __syncthreads();
+    }
+    const int incl = base + sm_scan[tid];
+    if (nt > 0 && want < incl && want >= incl - nt) {
+      const int p = die + 8 * (c0 + tid);
+      sm_pick[0] = p / a.num_kv_heads;
+      sm_pick[1] = p - sm_pick[0] * a.num_kv_heads;
+      sm_pick[2] = want - (incl - nt);            // place among the pair's tiles
+    }
+    base += sm_scan[kPThreads - 1];
+    __syncthreads();
+    if (sm_pick[0] >= 0 || want < base) break;
+  }
+}
+
 template <int R, int kD>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   static_assert(kD == 64 || kD == 128, "head_dim 64 or 128");
@@ -109,54 +160,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillSmem<kD> sm;
 
   const int tid = threadIdx.x;
-  // ---- which tile: the dies take (sequence, KV head) pairs round-robin -------
-  // Workgroups are handed to the eight dies (XCDs) round-robin by linear id,
-  // so linear id i runs on die i mod 8.  Die x works through the pairs x,
-  // x + 8, x + 16, ... one after the other, each pair's tiles heaviest first:
-  // every tile of a pair then runs on the die whose L2 already holds the
-  // pair's K/V, and with eight KV heads each die gets one head of every
-  // sequence, the same work.  The grid is an upper bound; surplus workgroups
-  // find no tile and leave.
   __shared__ int sm_scan[kPThreads];
   __shared__ int sm_pick[3];
-  {
-    const int lin = blockIdx.x;
-    const int die = lin & 7;
-    const int want = lin >> 3;                    // index in this die's queue of tiles
-    const int npairs = a.num_seqs * a.num_kv_heads;
-    const int mine = (npairs - die + 7) / 8;      // pairs die, die + 8, ...
-    if (tid == 0) sm_pick[0] = -1;
-    __syncthreads();
-    int base = 0;                                 // tiles of the die's earlier chunks
-    for (int c0 = 0; c0 < mine; c0 += kPThreads) {
-      int nt = 0;
-      if (c0 + tid < mine) {
-        const int ss = (die + 8 * (c0 + tid)) / a.num_kv_heads;
-        int q0, ql;
-        seq_rows(a, ss, q0, ql);
-        nt = (min(ql, a.max_q_len) + TQ - 1) / TQ;
-      }
-      // inclusive scan of the chunk's tile counts (Hillis-Steele in LDS)
-      sm_scan[tid] = nt;
-      __syncthreads();
-      for (int off = 1; off < kPThreads; off <<= 1) {
-        const int y = tid >= off ? sm_scan[tid - off] : 0;
-        __syncthreads();
-        sm_scan[tid] += y;
-        __syncthreads();
-      }
-      const int incl = base + sm_scan[tid];
-      if (nt > 0 && want < incl && want >= incl - nt) {
-        const int p = die + 8 * (c0 + tid);
-        sm_pick[0] = p / a.num_kv_heads;
-        sm_pick[1] = p - sm_pick[0] * a.num_kv_heads;
-        sm_pick[2] = want - (incl - nt);            // place among the pair's tiles
-      }
-      base += sm_scan[kPThreads - 1];
-      __syncthreads();
-      if (sm_pick[0] >= 0 || want < base) break;
-    }
-  }
+  pick_tile(a, TQ, sm_scan, sm_pick);
   if (sm_pick[0] < 0) return;
   const int s = sm_pick[0];
   const int g = sm_pick[1];
@@ -414,10 +420,253 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 pools: the same tiles and schedule on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32), with nothing rounded below fp32.
+//   S^T = K . Q^T : contraction step c takes d = c in the lower lane half and
+//                   d = c + D/2 in the upper one, so a lane reads its key's
+//                   K values four steps at a time from one LDS row and holds
+//                   one contiguous half of its column's q row.
+//   O^T += V^T . P^T: step r pairs the keys a = 8 (r / 4) + (r mod 4) (lower
+//                   half) and a + 4 (upper half), exactly the two keys whose
+//                   scores the lane holds in accumulator entry r, so P needs
+//                   no move; the lane reads V[its key][d] from LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+struct alignas(16) PrefillSmemF32 {
+  float k[2][kKeys][D + 4];           // K tile, [key][d]; rows 16 bytes apart mod 128
+  float v[2][kKeys][D + 4];           // V tile, [key][d]
+  int bad[2][2 * kHalves];
+};
+
+template <int R, int kD>
+__global__ __launch_bounds__(kPThreads) void prefill_f32_kernel(PrefillArgs a) {
+  static_assert(kD == 64 || kD == 128, "head_dim 64 or 128");
+  constexpr int NREP = 1 << R;
+  constexpr int TQ = kCols / NREP;    // tokens per tile
+  constexpr int kCPR = kD / 4;        // 16-byte chunks per K/V row
+  constexpr int kEPW = kCPR / 8;      // keys per lane and pass in the loader (4 or 2)
+  constexpr int kH = kD / 2;          // d values per lane half
+  __shared__ PrefillSmemF32<kD> sm;
+
+  const int tid = threadIdx.x;
+  __shared__ int sm_scan[kPThreads];
+  __shared__ int sm_pick[3];
+  pick_tile(a, TQ, sm_scan, sm_pick);
+  if (sm_pick[0] < 0) return;
+  const int s = sm_pick[0];
+  const int g = sm_pick[1];
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  int qs0, q_len;
+  seq_rows(a, s, qs0, q_len);
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
+  const int n_q = min(q_len, a.max_q_len);
+  const int row0 = qs0 + q_len - n_q;
+  const int n_tiles = (n_q + TQ - 1) / TQ;
+  const int tile = n_tiles - 1 - sm_pick[2];
+  if (tile < 0) return;
+  const int t0 = tile * TQ;
+  const int first_pos = L - n_q;
+
+  const int c = wave * 32 + col;
+  const int head = c / TQ;
+  const int tok = t0 + c % TQ;
+  const bool col_valid = tok < n_q;
+  const int qpos = first_pos + tok;
+  const int qh = g * NREP + head;
+
+  // Q^T as B operand: q[d = half * D/2 + c] for c = 0 .. D/2 - 1
+  float qf[kH];
+  {
+    const float* qrow = static_cast<const float*>(a.q) +
+                        (static_cast<int64_t>(row0 + (col_valid ? tok : 0)) * a.num_q_heads + qh) * kD +
+                        half * kH;
+#pragma unroll
+    for (int j = 0; j < kH / 4; ++j) {
+      float4 x = reinterpret_cast<const float4*>(qrow)[j];
+      if (!col_valid) x = make_float4(0.f, 0.f, 0.f, 0.f);
+      qf[4 * j] = x.x; qf[4 * j + 1] = x.y; qf[4 * j + 2] = x.z; qf[4 * j + 3] = x.w;
+    }
+  }
+
+  const int last_tok = min(t0 + TQ, n_q) - 1;
+  const int key_end = first_pos + last_tok + 1;
+  const int n_kt = key_end > 0 ? (key_end + kKeys - 1) / kKeys : 0;
+  const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const uint32_t row_bytes = a.geom.token_stride;
+  const uint32_t block_bytes = a.geom.span;
+
+  // loader: as the bf16 kernel, wave w loads keys 8 w .. 8 w + 7 of a tile
+  const int ld_key = 8 * wave + kEPW * (lane / kCPR);
+  const int ld_dc = lane % kCPR;
+  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  auto load_ids = [&](int kt, int (&ids)[kHalves]) {
+#pragma unroll
+    for (int ps = 0; ps < kHalves; ++ps) {
+      const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;
+      ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
+    }
+  };
+  uint4 kreg[kHalves][kEPW], vreg[kHalves][kEPW];
+  int kbad[kHalves];
+  auto fetch = [&](int kt, const int (&ids)[kHalves]) {
+#pragma unroll
+    for (int ps = 0; ps < kHalves; ++ps) {
+      const int phys = uniform(ids[ps]);
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      kbad[ps] = ok ? 0 : 1;
+      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
+      const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
+      const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
+#pragma unroll
+      for (int e = 0; e < kEPW; ++e) {
+        const int kpos = kt * kKeys + ld_key + 32 * ps + e;
+        const uint32_t off = kpos < L ? ld_off + e * row_bytes : block_bytes;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        kreg[ps][e] = make_uint4(kx[0], kx[1], kx[2], kx[3]);
+        vreg[ps][e] = make_uint4(vx[0], vx[1], vx[2], vx[3]);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int ps = 0; ps < kHalves; ++ps) {
+#pragma unroll
+      for (int e = 0; e < kEPW; ++e) {
+        const int key = ld_key + 32 * ps + e;
+        *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 4]) = kreg[ps][e];
+        *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 4]) = vreg[ps][e];
+      }
+      if ((wave & 1) == 0 && lane == 0) sm.bad[buf][(wave >> 1) + 2 * ps] = kbad[ps];
+    }
+  };
+
+  f32x16 o[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = kPNegBig, lsum = 0.f;
+  const float sl2 = a.scale_log2;
+  const int min_qpos = first_pos + t0;
+
+  int ids[kHalves];
+  if (n_kt > 0) {
+    load_ids(0, ids);
+    fetch(0, ids);
+    stash(0);
+    if (n_kt > 1) {
+      load_ids(1, ids);
+      fetch(1, ids);
+      if (n_kt > 2) load_ids(2, ids);
+    }
+  }
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) {
+      stash(buf ^ 1);
+      if (kt + 2 < n_kt) fetch(kt + 2, ids);
+    }
+#pragma unroll
+    for (int t = 0; t < kHalves; ++t) {
+      // ---- S^T = K . Q^T over D / 2 steps
+      f32x16 st;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < kH / 4; ++j) {
+        const float4 kx = *reinterpret_cast<const float4*>(&sm.k[buf][32 * t + col][half * kH + 4 * j]);
+        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qf[4 * j], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qf[4 * j + 1], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qf[4 * j + 2], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qf[4 * j + 3], st, 0, 0, 0);
+      }
+      // ---- causal mask, keys of blocks outside the pool, online softmax
+      const int key0 = kt * kKeys + 32 * t;
+      if (key0 + 31 > min_qpos) {
+        const int lim = qpos - key0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
+      }
+      const int bad0 = sm.bad[buf][2 * t], bad1 = sm.bad[buf][2 * t + 1];
+      if (bad0 | bad1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (r < 8 ? bad0 : bad1) st[r] = -INFINITY;
+      }
+      float tmax = st[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+      tmax = fmaxf(tmax, xor32(tmax)) * sl2;
+      if (__builtin_amdgcn_ballot_w64(tmax > m + kPRescale) != 0) {
+        const float m_new = tmax > m + kPRescale ? tmax : m;
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(st[r], sl2, -m));
+        lsum += p[r];
+      }
+      // ---- O^T += V^T . P^T, step r on keys a + 4 half, a = 8 (r / 4) + r mod 4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.v[buf][key][32 * dt + col], p[r], o[dt],
+                                                       0, 0, 0);
+      }
+    }
+    if (kt + 3 < n_kt) load_ids(kt + 3, ids);
+    __syncthreads();
+  }
+
+  lsum += xor32(lsum);
+  if (!col_valid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  float* orow = static_cast<float*>(a.out) + (static_cast<int64_t>(row0 + tok) * a.num_q_heads + qh) * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dt + 8 * r4 + 4 * half;
+      *reinterpret_cast<float4*>(orow + d) =
+          make_float4(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv, o[dt][4 * r4 + 2] * inv,
+                      o[dt][4 * r4 + 3] * inv);
+    }
+}
+
 }  // namespace
 
 template <int D>
 hipError_t launch_heads(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.dtype == 0) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+      case 1: return launch_kernel(prefill_f32_kernel<0, D>, grid, dim3(kPThreads), 0, stream, a);
+      case 2: return launch_kernel(prefill_f32_kernel<1, D>, grid, dim3(kPThreads), 0, stream, a);
+      case 4: return launch_kernel(prefill_f32_kernel<2, D>, grid, dim3(kPThreads), 0, stream, a);
+      case 8: return launch_kernel(prefill_f32_kernel<3, D>, grid, dim3(kPThreads), 0, stream, a);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.num_q_heads / a.num_kv_heads) {
     case 1: return launch_kernel(prefill_kernel<0, D>, grid, dim3(kPThreads), 0, stream, a);
     case 2: return launch_kernel(prefill_kernel<1, D>, grid, dim3(kPThreads), 0, stream, a);

@@ -158,9 +158,9 @@ def test_write_and_slot_mapping_checks(lib):
 
 def test_prefill_checks(lib):
     s = seqs()
-    f32 = pool(dtype=pa.PA_F32)
-    assert lib.pa_prefill(ctypes.byref(f32), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
-                          None) == pa.PA_ERR_UNSUPPORTED
+    f32 = pool(dtype=pa.PA_F32)       # fp32 pools are supported: a bad pointer still fails first
+    assert lib.pa_prefill(ctypes.byref(f32), ctypes.byref(s), FAKE, FAKE, 0, 10, 10, 8, 0.1,
+                          None) == pa.PA_ERR_INVALID_ARG
     d96 = pool(head_dim=96)
     assert lib.pa_prefill(ctypes.byref(d96), ctypes.byref(s), FAKE, FAKE, FAKE, 10, 10, 8, 0.1,
                           None) == pa.PA_ERR_UNSUPPORTED

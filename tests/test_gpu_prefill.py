@@ -164,13 +164,31 @@ def test_prefill_causal_bitwise():
     assert not torch.equal(first[cut + 1:].view(torch.int16), g2.out[cut + 1:].view(torch.int16))
 
 
-def test_prefill_unsupported_shapes_rejected():
-    w = wl.prefill_workload("prefill_f32", 622, dtype=wl.F32, num_q_heads=4, num_kv_heads=4,
-                            head_dim=64, block_size=16, num_blocks=16, context_lens=[10])
-    g = runner.GpuStep(w)
-    with pytest.raises(pa.PagedAttentionError) as e:
-        g.attend()
-    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("num_q_heads,num_kv_heads,head_dim", [
+    (12, 12, 64),     # the GPT-2 shape of the pages' model
+    (8, 2, 64), (16, 2, 64),
+    (4, 4, 128), (8, 4, 128), (16, 4, 128), (32, 4, 128),
+])
+def test_prefill_f32(num_q_heads, num_kv_heads, head_dim):
+    """fp32 pools, fp32 everywhere (tolerance 1e-5): whole prompts across the
+    32-token and 32-key tile edges, continued prompts, a decode row, and
+    more new tokens than the context holds."""
+    lens = [1, 7, 31, 32, 33, 64, 119, 300, 503, 129, 40, 5]
+    q_lens = [1, 7, 31, 32, 33, 64, 119, 300, 200, 1, 40, 9]
+    w = wl.prefill_workload(f"prefill_f32_{num_q_heads}_{num_kv_heads}_{head_dim}",
+                            700 + num_q_heads + head_dim, dtype=wl.F32, num_q_heads=num_q_heads,
+                            num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=16,
+                            num_blocks=512, context_lens=lens, q_lens=q_lens)
+    _full(w)
+
+
+def test_prefill_f32_gpt2_prompts():
+    """The GPT-2-shaped decode configurations' contexts (119, 503, 1015, 2039
+    tokens; 12 heads of 64) as whole fp32 prompts in one call."""
+    w = wl.prefill_workload("prefill_f32_gpt2", 710, dtype=wl.F32, num_q_heads=12, num_kv_heads=12,
+                            head_dim=64, block_size=16, num_blocks=512,
+                            context_lens=list(wl.GPT2_CONTEXTS))
+    _full(w)
 
 
 def test_mixed_decode_and_prefill_batch():
