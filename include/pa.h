@@ -98,7 +98,10 @@ typedef enum pa_layout {
  * least the dense block size and a multiple of 16 bytes.  Slots keep their
  * meaning in every layout: slot = block * block_size + offset in the block.
  *
- * Supported: block_size 16, head_dim 64 or 128, dtype PA_F32 or PA_BF16.
+ * Supported: block_size 8, 16, 32, 64, 128 or 256 (JuliaPagedAttn
+ * "API Reference" and Pico-vLLM's BlockManager both take the block size as
+ * a parameter), head_dim 64 or 128, dtype PA_F32 or PA_BF16.  The kernels
+ * walk a history in units of 16 tokens whatever the block size.
  */
 typedef struct pa_kv_pool {
   void* k_cache;
@@ -306,7 +309,8 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
  * arrival counters, then 2 * V * n_rep * head_dim floats of partial outputs
  * (padded to 256 bytes), then 2 * V * n_rep * 2 floats of (max, sum), with
  * V = min(2048, ceil(num_kv_heads * num_seqs * ceil(max_context_len / 16) /
- * (partition_size / 16))) the most slices a call can use.  Host only, needs
+ * (partition_size / 16))) the most slices a call can use (with
+ * max_context_len capped at max_blocks_per_seq * block_size).  Host only, needs
  * no device; returns 0 for invalid arguments too (pa_decode then reports
  * them).
  */
@@ -330,7 +334,7 @@ size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs
  * for bf16.  Accumulation is fp32.
  *
  * partition_size: 0 (or at least the longest context) = each (sequence, KV
- * head) pair in one pass.  Otherwise a multiple of block_size that turns on
+ * head) pair in one pass.  Otherwise a multiple of 16 that turns on
  * the split-context decode: the blocks of all pairs, laid end to end, are cut
  * into equal slices of at least partition_size tokens, one per workgroup that
  * the GPU holds at once, so every workgroup reads the same number of bytes

@@ -231,6 +231,10 @@ class KVPool:
     def num_blocks(self) -> int:
         return int(self.k_cache.shape[0])
 
+    @property
+    def block_size(self) -> int:
+        return _pool_geometry(self.k_cache, self.v_cache, self.layout)[1]
+
 
 @dataclass
 class SeqDesc:
@@ -312,7 +316,8 @@ def check_slots(slot_mapping, num_blocks: int, block_size: int = 16) -> None:
 
 def _validate_seqs(pool: KVPool, seqs: "SeqDesc") -> None:
     if validating():
-        check_tables(seqs.block_tables, seqs.context_lens, pool.num_blocks, seqs.max_context_len)
+        check_tables(seqs.block_tables, seqs.context_lens, pool.num_blocks, seqs.max_context_len,
+                     pool.block_size)
 
 
 def _check_q_start_loc(q_start_loc: torch.Tensor, num_seqs: int, num_tokens: int,
@@ -351,7 +356,7 @@ def pa_write_kv(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
                 slot_mapping: torch.Tensor, stream=None) -> None:
     lib = load_library()
     if validating():
-        check_slots(slot_mapping, pool.num_blocks)
+        check_slots(slot_mapping, pool.num_blocks, pool.block_size)
     _, _, H, D, _ = _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)
     T = slot_mapping.numel()
     for name, t in (("k_new", k_new), ("v_new", v_new)):

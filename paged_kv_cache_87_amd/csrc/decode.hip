@@ -289,7 +289,7 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 //
 // Plan in dynamic LDS: ctx[S] clamped context lengths, pre[S+1] exclusive
 // prefix sum of blocks per KV head.
-template <typename T, int D, int R>
+template <typename T, int D, int R, bool kSmall>
 __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(DecodeArgs a) {
   constexpr int kWaves = decode_waves<T, D, R>();
   constexpr int kThreads = 64 * kWaves;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       int L = a.context_lens[q];
       L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
       sm_ctx[q] = L;
-      cb += L > 0 ? (L + kBlockSize - 1) / kBlockSize + a.seg_cost : 0;
+      cb += L > 0 ? (L + kUnit - 1) / kUnit + a.seg_cost : 0;
     }
     sm_scan[tid] = cb;
     __syncthreads();
@@ -358,7 +358,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     int e = sm_scan[tid];
     for (int q = b0; q < b1; ++q) {
       sm_pre[q] = e;
-      e += sm_ctx[q] > 0 ? (sm_ctx[q] + kBlockSize - 1) / kBlockSize + a.seg_cost : 0;
+      e += sm_ctx[q] > 0 ? (sm_ctx[q] + kUnit - 1) / kUnit + a.seg_cost : 0;
     }
     __syncthreads();
   }
@@ -383,7 +383,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     F1 = static_cast<int>(f0 + Q < B ? f0 + Q : B);
   }
   const int C = a.seg_cost;
-  auto nb_of = [&](int q) { return (sm_ctx[q] + kBlockSize - 1) / kBlockSize; };
+  auto nb_of = [&](int q) { return (sm_ctx[q] + kUnit - 1) / kUnit; };
   auto cost_of = [&](int q) { return sm_pre[q + 1] - sm_pre[q]; };
   struct Seg {
     int s, g, L, tok1, blk0, blk1;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       x.slot = -1;
     }
     x.L = sm_ctx[x.s];
-    x.tok1 = min(x.blk1 * kBlockSize, x.L);
+    x.tok1 = min(x.blk1 * kUnit, x.L);
     return x;
   };
   auto skip_empty = [&](int p) {
@@ -433,11 +433,22 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     return split ? x.end : skip_empty(pos + gridDim.x);
   };
   const int pos_end = split ? F1 : n_pairs;
-  // lane t: table entry of this wave's t-th block of the chunk at c0
+  // lane t: table entries of this wave's t-th 16-token unit of the chunk at
+  // c0.  Unit j holds positions 16 j .. 16 j + 15: with blocks of 16 tokens
+  // or more, the rows 16 j mod B .. of block 16 j / B; with blocks of 8, two
+  // blocks, 2 j and 2 j + 1 (.y; the same block as .x otherwise)
+  const uint32_t bshift = a.geom.block_shift;
+  constexpr bool small = kSmall;     // blocks of 8 tokens (block_shift 3)
   auto load_tbl = [&](const Seg& x, int c0) {
     const int j = c0 + wave + kWaves * lane;
-    const int lim = min(x.blk1, a.max_blocks_per_seq);
-    return j < lim ? a.block_tables[static_cast<int64_t>(x.s) * a.max_blocks_per_seq + j] : -1;
+    const int e = (j << 4) >> bshift;
+    const int32_t* row = a.block_tables + static_cast<int64_t>(x.s) * a.max_blocks_per_seq;
+    int2 t = make_int2(-1, -1);
+    if (j < x.blk1) {
+      t.x = e < a.max_blocks_per_seq ? row[e] : -1;
+      if constexpr (small) t.y = e + 1 < a.max_blocks_per_seq ? row[e + 1] : -1;
+    }
+    return t;
   };
   const int own = li >> (4 - R);     // head whose full score this lane ends with
   // query rows of the segment's heads, in this lane's scatter order
@@ -473,7 +484,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   if (cur.blk1 <= cur.blk0) return;  // the slice holds no block
   int c0 = cur.blk0;                 // first block of the current chunk
   int nk = 0;                        // this wave's blocks in the current chunk
-  int tbl = load_tbl(cur, c0);
+  int2 tbl = load_tbl(cur, c0);
   uint32_t qv[N][NW];
   load_q(cur, qv);
   uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
@@ -493,30 +504,46 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
 
-  // Issue the loads of this wave's k-th block of the current chunk into
-  // (kf, vf) and return its number of valid tokens.  Past the wave's last
-  // block, or for a table entry outside the pool, the descriptors have size
-  // 0: the loads return zeros without touching memory and the block counts 0
-  // valid tokens.
+  // Issue the loads of this wave's k-th unit of the current chunk into
+  // (kf, vf) and return the mask of its valid tokens (bit t: token 16 j + t).
+  // Past the wave's last unit, or for a table entry outside the pool, the
+  // descriptors have size 0: the loads return zeros without touching memory
+  // and the tokens of that block count as invalid.  Token rows 0 .. 7 of the
+  // unit (uu = 0, 1) come through the first descriptor, rows 8 .. 15 through
+  // the second, which is the first one again unless blocks hold 8 tokens.
   auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
-    int phys = -1;
+    int phys = -1, phys2 = -1;
     int nvalid = 0;
+    int sub = 0;                     // first token row of the unit inside its block
     if (k < nk) {
       const int j = c0 + wave + kWaves * k;
-      phys = __builtin_amdgcn_readlane(tbl, k);
-      const int n = cur.tok1 - j * kBlockSize;
-      nvalid = n < kBlockSize ? n : kBlockSize;
+      phys = __builtin_amdgcn_readlane(tbl.x, k);
+      phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
+      const int n = cur.tok1 - j * kUnit;
+      nvalid = n < kUnit ? n : kUnit;
+      sub = small ? 0 : (j << 4) & ((1 << bshift) - 1);
     }
     const bool ok = phys >= 0 && phys < a.num_blocks;
-    if (!ok) nvalid = 0;
-    const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride : 0;
-    const Rsrc rk = make_rsrc(kpool + off, ok ? block_bytes : 0u);
-    const Rsrc rv = make_rsrc(vpool + off, ok ? block_bytes : 0u);
+    const bool ok2 = phys2 >= 0 && phys2 < a.num_blocks;
+    const int vmask = ((ok ? 0x00ff : 0) | (ok2 ? 0xff00 : 0)) & ((1 << nvalid) - 1);
+    const uint32_t sub_bytes = static_cast<uint32_t>(sub) * row_bytes;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride + sub_bytes : 0;
+    const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
+    const Rsrc rk = make_rsrc(kpool + off, size);
+    const Rsrc rv = make_rsrc(vpool + off, size);
+    const int64_t off2 = ok2 ? static_cast<int64_t>(phys2) * block_stride : 0;
+    const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
+    const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
+    const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
+    for (int uu = 0; uu < 2; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
 #pragma unroll
-    for (int uu = 0; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
-    return nvalid;
+    for (int uu = 2; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
+#pragma unroll
+    for (int uu = 2; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
+    return vmask;
   };
 
   // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
@@ -524,7 +551,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   // when a score passes it by more than kRescaleLog2 (then the accumulators
   // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
   // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
-  auto process = [&](F (&kf)[4], F (&vf)[4], int nvalid) {
+  auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
     float z[4];
 #pragma unroll
     for (int uu = 0; uu < 4; ++uu) {
@@ -533,13 +560,13 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
       z[uu] = reduce_scatter<R>(part_dot) * sl2;
     }
-    // tokens past the context (partial last block, or a block the ring runs
-    // past its end) get no weight and a zero value row, whatever the pool
-    // holds there
-    if (nvalid < kBlockSize) {
+    // tokens past the context (partial last unit, or a unit the ring runs
+    // past its end) or in a block outside the pool get no weight and a zero
+    // value row, whatever the pool holds there
+    if (vmask != 0xffff) {
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu) {
-        if (row + 4 * uu >= nvalid) {
+        if (((vmask >> (row + 4 * uu)) & 1) == 0) {
           z[uu] = -INFINITY;
 #pragma unroll
           for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
@@ -624,7 +651,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   bool has_next = pos_n < pos_end;
   Seg nxt = has_next ? seg_at(pos_n) : cur;
   has_next = has_next && nxt.blk1 > nxt.blk0;
-  int tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
+  int2 tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
   nk = chunk_blocks(cur, c0);
 
   F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
@@ -758,7 +785,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     }
     tbl = tbl_nxt;
     load_q(cur, qv);
-    tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : -1;
+    tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
     c0 = cur.blk0;
     nk = chunk_blocks(cur, c0);
     lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
@@ -828,10 +855,10 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
 
 // The persistent grid: what the device holds at once, but no more
 // workgroups than there are slices (split) or pairs (whole pairs).
-template <typename T, int D, int R>
+template <typename T, int D, int R, bool kSmall>
 hipError_t grid_typed(const DecodeArgs& a, int* grid) {
   const size_t lds = plan_lds_bytes(a.num_seqs);
-  const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R>);
+  const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R, kSmall>);
   int resident = 0;
   constexpr int kThreads = 64 * decode_waves<T, D, R>();
   hipError_t e = resident_workgroups(fn, kThreads, lds, &resident);
@@ -843,39 +870,46 @@ hipError_t grid_typed(const DecodeArgs& a, int* grid) {
   return hipSuccess;
 }
 
-template <typename T, int D, int R>
+template <typename T, int D, int R, bool kSmall>
 hipError_t run_typed(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   int grid = 0;
-  const hipError_t e = grid_typed<T, D, R>(a, &grid);
+  const hipError_t e = grid_typed<T, D, R, kSmall>(a, &grid);
   if (e != hipSuccess) return e;
   if (grid_only != nullptr) {
     *grid_only = grid;
     return hipSuccess;
   }
   constexpr int kThreads = 64 * decode_waves<T, D, R>();
-  return launch_kernel(decode_kernel<T, D, R>, dim3(grid), dim3(kThreads),
+  return launch_kernel(decode_kernel<T, D, R, kSmall>, dim3(grid), dim3(kThreads),
                        plan_lds_bytes(a.num_seqs), stream, a);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kSmall>
 hipError_t run_heads(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return run_typed<T, D, 0>(a, stream, grid_only);
-    case 2: return run_typed<T, D, 1>(a, stream, grid_only);
-    case 4: return run_typed<T, D, 2>(a, stream, grid_only);
-    case 8: return run_typed<T, D, 3>(a, stream, grid_only);
+    case 1: return run_typed<T, D, 0, kSmall>(a, stream, grid_only);
+    case 2: return run_typed<T, D, 1, kSmall>(a, stream, grid_only);
+    case 4: return run_typed<T, D, 2, kSmall>(a, stream, grid_only);
+    case 8: return run_typed<T, D, 3, kSmall>(a, stream, grid_only);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Blocks of 8 tokens hold half a 16-token unit: a variant of their own.
+template <typename T, int D>
+hipError_t run_blocks(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
+  return a.geom.block_shift < 4 ? run_heads<T, D, true>(a, stream, grid_only)
+                                : run_heads<T, D, false>(a, stream, grid_only);
 }
 
 // Launch the decode, or with grid_only set only report the grid it would use.
 hipError_t run(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   if (a.dtype == 1) {
-    if (a.head_dim == 128) return run_heads<uint16_t, 128>(a, stream, grid_only);
-    if (a.head_dim == 64) return run_heads<uint16_t, 64>(a, stream, grid_only);
+    if (a.head_dim == 128) return run_blocks<uint16_t, 128>(a, stream, grid_only);
+    if (a.head_dim == 64) return run_blocks<uint16_t, 64>(a, stream, grid_only);
   } else {
-    if (a.head_dim == 128) return run_heads<float, 128>(a, stream, grid_only);
-    if (a.head_dim == 64) return run_heads<float, 64>(a, stream, grid_only);
+    if (a.head_dim == 128) return run_blocks<float, 128>(a, stream, grid_only);
+    if (a.head_dim == 64) return run_blocks<float, 64>(a, stream, grid_only);
   }
   return hipErrorInvalidValue;
 }

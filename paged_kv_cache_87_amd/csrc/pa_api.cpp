@@ -51,8 +51,10 @@ pa_status check_pool(const pa_kv_pool* pool) {
                 pool->num_kv_heads, pool->head_dim);
   if (pool->dtype != PA_F32 && pool->dtype != PA_BF16)
     return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", pool->dtype);
-  if (pool->block_size != pa::kBlockSize)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16)", pool->block_size);
+  if (pool->block_size < 8 || pool->block_size > 256 ||
+      (pool->block_size & (pool->block_size - 1)) != 0)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64, 128, 256)",
+                pool->block_size);
   if (pool->head_dim != 64 && pool->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", pool->head_dim);
   if (pool->num_kv_heads > 4096)
@@ -89,6 +91,8 @@ pa::PoolGeom geom_of(const pa_kv_pool* p) {
     g.token_stride = row;
     g.head_stride = static_cast<uint32_t>(p->block_size) * row;
   }
+  g.block_shift = 0;
+  while ((1 << g.block_shift) < p->block_size) ++g.block_shift;
   return g;
 }
 
@@ -98,7 +102,7 @@ size_t extent_bytes(const pa_kv_pool* p) {
   return static_cast<size_t>(g.block_stride) * (p->num_blocks - 1) + g.span;
 }
 
-pa_status check_seqs(const pa_seq_desc* seqs) {
+pa_status check_seqs(const pa_seq_desc* seqs, int32_t block_size) {
   if (seqs == nullptr) return fail(PA_ERR_INVALID_ARG, "sequence descriptor is null");
   if (seqs->num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", seqs->num_seqs);
   if (seqs->num_seqs > 0 && (seqs->block_tables == nullptr || seqs->context_lens == nullptr))
@@ -108,7 +112,7 @@ pa_status check_seqs(const pa_seq_desc* seqs) {
                 seqs->max_blocks_per_seq);
   if (seqs->max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG, "max_context_len %d < 0", seqs->max_context_len);
-  if (static_cast<int64_t>(seqs->max_blocks_per_seq) * pa::kBlockSize > INT32_MAX)
+  if (static_cast<int64_t>(seqs->max_blocks_per_seq) * block_size > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq too large");
   return PA_OK;
 }
@@ -144,8 +148,8 @@ bool device_addressable(const void* p, size_t bytes, bool host) {
   return true;
 }
 
-int32_t context_cap(const pa_seq_desc* seqs) {
-  const int64_t by_table = static_cast<int64_t>(seqs->max_blocks_per_seq) * pa::kBlockSize;
+int32_t context_cap(const pa_seq_desc* seqs, int32_t block_size) {
+  const int64_t by_table = static_cast<int64_t>(seqs->max_blocks_per_seq) * block_size;
   return static_cast<int32_t>(seqs->max_context_len < by_table ? seqs->max_context_len : by_table);
 }
 
@@ -193,17 +197,18 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
   return hipSuccess;
 }
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                       int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
-                       int32_t partition_size) {
+DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t max_context_len, int32_t num_kv_heads, int32_t num_q_heads,
+                       int32_t head_dim, int32_t partition_size) {
   DecodePlan p{};
-  const int64_t by_table = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
+  const int64_t by_table = static_cast<int64_t>(max_blocks_per_seq) * block_size;
   p.context_cap = static_cast<int32_t>(max_context_len < by_table ? max_context_len : by_table);
-  const int64_t cap_blocks = (static_cast<int64_t>(p.context_cap) + kBlockSize - 1) / kBlockSize;
+  // the kernel walks 16-token units
+  const int64_t cap_blocks = (static_cast<int64_t>(p.context_cap) + kUnit - 1) / kUnit;
   p.max_blocks = static_cast<int64_t>(num_kv_heads) * num_seqs * cap_blocks;
-  const int64_t cover = (cap_blocks > 0 ? cap_blocks : 1) * kBlockSize;
+  const int64_t cover = (cap_blocks > 0 ? cap_blocks : 1) * kUnit;
   if (partition_size <= 0 || partition_size >= cover) return p;   // no split
-  p.min_slice_blocks = partition_size / kBlockSize;
+  p.min_slice_blocks = partition_size / kUnit;
   const int64_t slices = (p.max_blocks + p.min_slice_blocks - 1) / p.min_slice_blocks;
   p.max_blocks += static_cast<int64_t>(num_kv_heads) * num_seqs * kSegCost;   // work range
   p.max_slices = static_cast<int32_t>(slices < kMaxSlices ? (slices > 0 ? slices : 1)
@@ -241,7 +246,7 @@ pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
   clear_error();
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_seqs(seqs, pool->block_size)) != PA_OK) return st;
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (slot_mapping == nullptr) return fail(PA_ERR_INVALID_ARG, "slot_mapping is null");
@@ -249,8 +254,9 @@ pa_status pa_slot_mapping(const pa_kv_pool* pool, const pa_seq_desc* seqs,
   if (q_start_loc == nullptr && num_tokens != seqs->num_seqs)
     return fail(PA_ERR_INVALID_ARG, "without q_start_loc num_tokens (%d) must equal num_seqs (%d)",
                 num_tokens, seqs->num_seqs);
-  pa::SlotMappingArgs a{seqs->block_tables, seqs->context_lens, q_start_loc, slot_mapping,
-                        seqs->num_seqs, seqs->max_blocks_per_seq, num_tokens, pool->num_blocks};
+  pa::SlotMappingArgs a{geom_of(pool).block_shift, seqs->block_tables, seqs->context_lens,
+                        q_start_loc, slot_mapping, seqs->num_seqs, seqs->max_blocks_per_seq,
+                        num_tokens, pool->num_blocks};
   return hip_status(pa::launch_slot_mapping(a, stream), "slot_mapping launch");
 }
 
@@ -277,7 +283,7 @@ pa_status pa_append_kv(const pa_kv_pool* pool, const pa_seq_desc* seqs, const vo
   clear_error();
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_seqs(seqs, pool->block_size)) != PA_OK) return st;
   if (seqs->num_seqs == 0) return PA_OK;
   if (k_new == nullptr || v_new == nullptr)
     return fail(PA_ERR_INVALID_ARG, "k_new or v_new is null");
@@ -356,12 +362,14 @@ size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs
                                  int32_t num_q_heads, int32_t partition_size) {
   if (pool == nullptr || seqs == nullptr || seqs->num_seqs < 0 ||
       seqs->max_blocks_per_seq <= 0 || seqs->max_context_len < 0 || pool->num_kv_heads <= 0 ||
-      pool->head_dim <= 0 || pool->block_size != pa::kBlockSize || num_q_heads <= 0 ||
+      pool->head_dim <= 0 || pool->block_size < 8 || pool->block_size > 256 ||
+      (pool->block_size & (pool->block_size - 1)) != 0 || num_q_heads <= 0 ||
       num_q_heads % pool->num_kv_heads != 0 || partition_size < 0 ||
-      partition_size % pool->block_size != 0)
+      partition_size % pa::kUnit != 0)
     return 0;
-  return pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, seqs->max_context_len,
-                         pool->num_kv_heads, num_q_heads, pool->head_dim, partition_size)
+  return pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, pool->block_size,
+                         seqs->max_context_len, pool->num_kv_heads, num_q_heads, pool->head_dim,
+                         partition_size)
       .workspace_bytes;
 }
 
@@ -377,19 +385,20 @@ pa_status prepare_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const 
                          bool io, pa::DecodeArgs* a, pa::DecodePlan* plan) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_seqs(seqs, pool->block_size)) != PA_OK) return st;
   if ((st = check_heads(pool, num_q_heads)) != PA_OK) return st;
-  if (partition_size < 0 || partition_size % pool->block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a multiple of block_size %d",
-                partition_size, pool->block_size);
+  if (partition_size < 0 || partition_size % pa::kUnit != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a multiple of %d",
+                partition_size, pa::kUnit);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
   if (io && seqs->num_seqs > 0) {
     if (q == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "q or out is null");
     if (!aligned16(q) || !aligned16(out))
       return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   }
-  *plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, seqs->max_context_len,
-                          pool->num_kv_heads, num_q_heads, pool->head_dim, partition_size);
+  *plan = pa::plan_decode(seqs->num_seqs, seqs->max_blocks_per_seq, pool->block_size,
+                          seqs->max_context_len, pool->num_kv_heads, num_q_heads, pool->head_dim,
+                          partition_size);
   if (plan->max_blocks >= (int64_t(1) << 31))
     return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * num_seqs * context blocks = %lld (below 2^31)",
                 static_cast<long long>(plan->max_blocks));
@@ -566,7 +575,7 @@ pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
   for (int s = 0; s < seqs->num_seqs; ++s) {
     int L = host_context_lens[s];
     L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
-    if (L > 0) B += static_cast<int64_t>(H) * ((L + pa::kBlockSize - 1) / pa::kBlockSize + C);
+    if (L > 0) B += static_cast<int64_t>(H) * ((L + pa::kUnit - 1) / pa::kUnit + C);
   }
   int64_t Q = 0;
   if (a.min_slice_blocks > 0) {
@@ -580,7 +589,7 @@ pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
     int L = host_context_lens[s];
     L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
     if (L == 0) continue;
-    const int64_t nb = (L + pa::kBlockSize - 1) / pa::kBlockSize;
+    const int64_t nb = (L + pa::kUnit - 1) / pa::kUnit;
     for (int g = 0; g < H; ++g) {
       const int64_t A = H * pre + g * (nb + C) + C;   // work position of the pair's block 0
       const int64_t n = Q > 0 ? (A + nb - 1) / Q - A / Q + 1 : 1;
@@ -602,7 +611,7 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
   clear_error();
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if ((st = check_seqs(seqs)) != PA_OK) return st;
+  if ((st = check_seqs(seqs, pool->block_size)) != PA_OK) return st;
   if ((st = check_heads(pool, num_q_heads)) != PA_OK) return st;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
   if (total_q_tokens < 0 || max_q_len < 0)
@@ -627,7 +636,7 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
   a.num_q_heads = num_q_heads;
   a.head_dim = pool->head_dim;
   a.max_blocks_per_seq = seqs->max_blocks_per_seq;
-  a.context_cap = context_cap(seqs);
+  a.context_cap = context_cap(seqs, pool->block_size);
   a.max_q_len = max_q_len;
   a.total_q_tokens = total_q_tokens;
   a.dtype = pool->dtype;

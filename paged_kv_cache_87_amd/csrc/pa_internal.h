@@ -26,7 +26,10 @@ inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, size_t
 void clear_report();
 pa_status report(pa_status status, const char* fmt, ...);
 
-constexpr int kBlockSize = 16;  // tokens per physical block the kernels handle
+// The kernels walk a sequence's history in units of 16 tokens: unit j holds
+// positions 16 j .. 16 j + 15.  A block of 16 or more tokens (a power of
+// two) holds whole units; a block of 8 tokens holds half of one.
+constexpr int kUnit = 16;
 
 // Where a (block, token, KV head) row of head_dim elements sits in a pool, in
 // bytes: block * block_stride + token * token_stride + head * head_stride.
@@ -36,9 +39,11 @@ struct PoolGeom {
   uint32_t token_stride;   // token-major: num_kv_heads * head row; head-major: one head row
   uint32_t head_stride;    // token-major: one head row; head-major: block_size head rows
   uint32_t span;           // block_size * num_kv_heads * head_dim * element size
+  uint32_t block_shift;    // log2(block_size), 3 .. 8
 };
 
 struct SlotMappingArgs {
+  uint32_t block_shift;        // log2(block_size)
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* q_start_loc;  // may be null (one token per sequence)
@@ -182,8 +187,8 @@ struct DecodePlan {
   size_t part_ml_offset;
   int64_t max_blocks;        // num_kv_heads * num_seqs * (ceil(context_cap / block size) + segment price)
 };
-DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
-                       int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
-                       int32_t partition_size);
+DecodePlan plan_decode(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t max_context_len, int32_t num_kv_heads, int32_t num_q_heads,
+                       int32_t head_dim, int32_t partition_size);
 
 }  // namespace pa

@@ -73,7 +73,7 @@ template <int D>
 struct alignas(16) PrefillSmem {
   uint16_t k[2][kKeys][kKStride<D>];  // K tile, [key][d]
   uint16_t v[2][kKeys][kVStride<D>];  // V tile, [key][d]
-  int bad[2][2 * kHalves];            // per 16-key block of a tile: its table entry is not a block
+  int bad[2][4 * kHalves];            // per 8-key group of a tile: its table entry is not a block
 };
 
 // The q / out rows of sequence s: [q0, q0 + q_len), q_start_loc clamped to
@@ -228,14 +228,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // no weight, as the decode skips such blocks
   const int ld_key = 8 * wave + kEPW * (lane / kCPR);   // first of the lane's keys
   const int ld_dc = lane % kCPR;                         // 8-element chunk of d
-  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
+  // offset of the lane's first key and chunk from the wave's first key (the
+  // wave's 8 keys are consecutive rows of one block at any block size >= 8)
+  const uint32_t ld_off = (ld_key - 8 * wave) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
+  const uint32_t bshift = a.geom.block_shift;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   auto load_ids = [&](int kt, int (&ids)[kHalves]) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps) {
       const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;   // the wave's first key this pass
-      ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
+      ids[ps] = kpos0 < L ? table[kpos0 >> bshift] : -1;
     }
   };
   uint4 kreg[kHalves][kEPW], vreg[kHalves][kEPW];  // [pass][key of the lane's run]
@@ -246,13 +249,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       const int phys = uniform(ids[ps]);
       const bool ok = phys >= 0 && phys < a.num_blocks;
       kbad[ps] = ok ? 0 : 1;
-      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
-      const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
-      const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
+      const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;    // the wave's first key
+      const uint32_t sub_bytes =
+          static_cast<uint32_t>(kpos0 & ((1 << bshift) - 1)) * row_bytes;
+      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride + sub_bytes : 0;
+      const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
+      const Rsrc rk = make_rsrc(kpool + boff, size);
+      const Rsrc rv = make_rsrc(vpool + boff, size);
 #pragma unroll
       for (int e = 0; e < kEPW; ++e) {
         const int kpos = kt * kKeys + ld_key + 32 * ps + e;
-        const uint32_t off = kpos < L ? ld_off + e * row_bytes : block_bytes;
+        const uint32_t off = kpos < L ? ld_off + e * row_bytes : size;
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
@@ -270,8 +277,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 8]) = kreg[ps][e];
         *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 8]) = vreg[ps][e];
       }
-      // waves 0 and 2 load the first keys of the tile's two blocks
-      if ((wave & 1) == 0 && lane == 0) sm.bad[buf][(wave >> 1) + 2 * ps] = kbad[ps];
+      // wave w loads the tile's keys 8 w .. 8 w + 7
+      if (lane == 0) sm.bad[buf][wave + 4 * ps] = kbad[ps];
     }
   };
   // transposing-read source address of this lane: key row 4 * half + (lane % 16) / 4,
@@ -342,12 +349,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
           if (8 * (r >> 2) + (r & 3) > lim) st[t][r] = -INFINITY;
       }
       // keys of a block whose table entry is not in the pool get no weight
-      // (rows r < 8 are the half's first 16 keys, r >= 8 its second 16)
-      const int bad0 = sm.bad[buf][2 * t], bad1 = sm.bad[buf][2 * t + 1];
-      if (bad0 | bad1) {
+      const int4 bad = *reinterpret_cast<const int4*>(&sm.bad[buf][4 * t]);
+      if (bad.x | bad.y | bad.z | bad.w) {
+        // accumulator entry r holds a key of the group r / 4
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r < 8 ? bad0 : bad1) st[t][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int b = (r >> 2) == 0 ? bad.x : (r >> 2) == 1 ? bad.y : (r >> 2) == 2 ? bad.z : bad.w;
+          if (b) st[t][r] = -INFINITY;
+        }
       }
       float tmax = st[t][0];
 #pragma unroll
@@ -436,7 +445,7 @@ template <int D>
 struct alignas(16) PrefillSmemF32 {
   float k[2][kKeys][D + 4];           // K tile, [key][d]; rows 16 bytes apart mod 128
   float v[2][kKeys][D + 4];           // V tile, [key][d]
-  int bad[2][2 * kHalves];
+  int bad[2][4 * kHalves];
 };
 
 template <int R, int kD>
@@ -504,14 +513,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_f32_kernel(PrefillArgs a) {
   // loader: as the bf16 kernel, wave w loads keys 8 w .. 8 w + 7 of a tile
   const int ld_key = 8 * wave + kEPW * (lane / kCPR);
   const int ld_dc = lane % kCPR;
-  const uint32_t ld_off = (ld_key % kBlockSize) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
+  // offset of the lane's first key and chunk from the wave's first key (the
+  // wave's 8 keys are consecutive rows of one block at any block size >= 8)
+  const uint32_t ld_off = (ld_key - 8 * wave) * row_bytes + g * a.geom.head_stride + ld_dc * 16;
+  const uint32_t bshift = a.geom.block_shift;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   auto load_ids = [&](int kt, int (&ids)[kHalves]) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps) {
       const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;
-      ids[ps] = kpos0 < L ? table[kpos0 / kBlockSize] : -1;
+      ids[ps] = kpos0 < L ? table[kpos0 >> bshift] : -1;
     }
   };
   uint4 kreg[kHalves][kEPW], vreg[kHalves][kEPW];
@@ -522,13 +534,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_f32_kernel(PrefillArgs a) {
       const int phys = uniform(ids[ps]);
       const bool ok = phys >= 0 && phys < a.num_blocks;
       kbad[ps] = ok ? 0 : 1;
-      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride : 0;
-      const Rsrc rk = make_rsrc(kpool + boff, ok ? block_bytes : 0u);
-      const Rsrc rv = make_rsrc(vpool + boff, ok ? block_bytes : 0u);
+      const int kpos0 = kt * kKeys + 8 * wave + 32 * ps;    // the wave's first key
+      const uint32_t sub_bytes =
+          static_cast<uint32_t>(kpos0 & ((1 << bshift) - 1)) * row_bytes;
+      const int64_t boff = ok ? static_cast<int64_t>(phys) * a.geom.block_stride + sub_bytes : 0;
+      const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
+      const Rsrc rk = make_rsrc(kpool + boff, size);
+      const Rsrc rv = make_rsrc(vpool + boff, size);
 #pragma unroll
       for (int e = 0; e < kEPW; ++e) {
         const int kpos = kt * kKeys + ld_key + 32 * ps + e;
-        const uint32_t off = kpos < L ? ld_off + e * row_bytes : block_bytes;
+        const uint32_t off = kpos < L ? ld_off + e * row_bytes : size;
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
@@ -546,7 +562,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_f32_kernel(PrefillArgs a) {
         *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 4]) = kreg[ps][e];
         *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 4]) = vreg[ps][e];
       }
-      if ((wave & 1) == 0 && lane == 0) sm.bad[buf][(wave >> 1) + 2 * ps] = kbad[ps];
+      if (lane == 0) sm.bad[buf][wave + 4 * ps] = kbad[ps];
     }
   };
 
@@ -599,11 +615,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_f32_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > lim) st[r] = -INFINITY;
       }
-      const int bad0 = sm.bad[buf][2 * t], bad1 = sm.bad[buf][2 * t + 1];
-      if (bad0 | bad1) {
+      const int4 bad = *reinterpret_cast<const int4*>(&sm.bad[buf][4 * t]);
+      if (bad.x | bad.y | bad.z | bad.w) {
+        // accumulator entry r holds a key of the group r / 4
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r < 8 ? bad0 : bad1) st[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int b = (r >> 2) == 0 ? bad.x : (r >> 2) == 1 ? bad.y : (r >> 2) == 2 ? bad.z : bad.w;
+          if (b) st[r] = -INFINITY;
+        }
       }
       float tmax = st[0];
 #pragma unroll

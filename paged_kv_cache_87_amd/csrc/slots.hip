@@ -1,9 +1,9 @@
 // Slot mapping and the slot-mapped K/V write (gfx950).
 //
 // A token at position `pos` of sequence `s` lives in logical block
-// pos / 16 at offset pos % 16; the block table maps the logical block to a
-// physical block, and the token's slot is the flat row
-// physical * 16 + offset of the pool viewed as [num_blocks * 16, Hkv, D]
+// pos / B at offset pos % B (B = block_size); the block table maps the
+// logical block to a physical block, and the token's slot is the flat row
+// physical * B + offset of the pool viewed as [num_blocks * B, Hkv, D]
 // (JuliaPagedAttn README, "Project Structure": slot mapping in the cache
 // layout; nanoserve Day 19, "Diagram": slot_mapping).  The write copies each
 // new token's [Hkv, D] row into its slot bit for bit (JuliaPagedAttn "API
@@ -22,16 +22,18 @@ constexpr int kSlotThreads = 256;
 constexpr int kWriteThreads = 256;
 
 // Slot of position `pos` of sequence `s` whose context is `L` tokens: the
-// table's block for pos / 16, offset pos % 16; -1 when the position is not in
-// the context or the table entry is not a block of the pool.
+// table's block for pos / block_size, offset pos % block_size (block_size =
+// 2^shift); -1 when the position is not in the context or the table entry is
+// not a block of the pool.
 __device__ __forceinline__ int64_t slot_of(const int32_t* block_tables, int max_blocks_per_seq,
-                                           int num_blocks, int s, int L, int pos) {
+                                           int num_blocks, uint32_t shift, int s, int L,
+                                           int pos) {
   if (pos < 0 || pos >= L) return -1;
-  const int logical = pos / kBlockSize;
+  const int logical = pos >> shift;
   if (logical >= max_blocks_per_seq) return -1;
   const int phys = block_tables[static_cast<int64_t>(s) * max_blocks_per_seq + logical];
   if (phys < 0 || phys >= num_blocks) return -1;
-  return static_cast<int64_t>(phys) * kBlockSize + (pos % kBlockSize);
+  return (static_cast<int64_t>(phys) << shift) + (pos & ((1 << shift) - 1));
 }
 
 __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingArgs a) {
@@ -56,8 +58,8 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(SlotMappingA
   }
   const int L = a.context_lens[s];
   a.slot_mapping[i] = idx >= 0 && idx < q_len
-                          ? slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks, s, L,
-                                    L - q_len + idx)
+                          ? slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks,
+                                    a.block_shift, s, L, L - q_len + idx)
                           : -1;
 }
 
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(kWriteThreads) void write_kv_kernel(WriteKVArgs a) 
   if (slot < 0 || slot >= a.num_slots) return;
   const int h = part / chunks_per_head;
   const int q = part - h * chunks_per_head;
-  const int64_t blk = slot / kBlockSize;
-  const int in_blk = static_cast<int>(slot - blk * kBlockSize);
+  const int64_t blk = slot >> a.geom.block_shift;
+  const int in_blk = static_cast<int>(slot - (blk << a.geom.block_shift));
   const int64_t dst_off = blk * a.geom.block_stride +
                           static_cast<int64_t>(in_blk) * a.geom.token_stride +
                           static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;
@@ -105,13 +107,14 @@ __global__ __launch_bounds__(kWriteThreads) void append_kv_kernel(AppendKVArgs a
   const uint4* src = static_cast<const uint4*>(blockIdx.y == 0 ? a.k_new : a.v_new);
   const uint4 val = src[static_cast<int64_t>(t) * chunks_per_row + part];
   const int L = a.context_lens[t];
-  const int64_t slot = slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks, t, L, L - 1);
+  const int64_t slot = slot_of(a.block_tables, a.max_blocks_per_seq, a.num_blocks,
+                               a.geom.block_shift, t, L, L - 1);
   if (part == 0 && blockIdx.y == 0 && a.slot_mapping != nullptr) a.slot_mapping[t] = slot;
   if (slot < 0) return;
   const int h = part / chunks_per_head;
   const int q = part - h * chunks_per_head;
-  const int64_t blk = slot / kBlockSize;
-  const int in_blk = static_cast<int>(slot - blk * kBlockSize);
+  const int64_t blk = slot >> a.geom.block_shift;
+  const int in_blk = static_cast<int>(slot - (blk << a.geom.block_shift));
   const int64_t dst_off = blk * a.geom.block_stride +
                           static_cast<int64_t>(in_blk) * a.geom.token_stride +
                           static_cast<int64_t>(h) * a.geom.head_stride + 16 * q;

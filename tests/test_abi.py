@@ -84,7 +84,9 @@ def decode(lib, p, s, q=FAKE, out=FAKE, hq=8, scale=0.1, part=0, ws=None, ws_byt
     (dict(v_cache=FAKE + 8), pa.PA_ERR_INVALID_ARG),        # misaligned
     (dict(num_blocks=0), pa.PA_ERR_INVALID_ARG),
     (dict(dtype=7), pa.PA_ERR_INVALID_ARG),
-    (dict(block_size=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=12), pa.PA_ERR_UNSUPPORTED),              # not a power of two
+    (dict(block_size=512), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=4), pa.PA_ERR_UNSUPPORTED),
     (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_pools(lib, change, status):
@@ -244,7 +246,7 @@ def test_split_info_rejects_bad_arguments(lib):
                                     None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), None, 8, 0,
                                     ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
-    assert lib.pa_decode_split_info(ctypes.byref(pool(block_size=32)), ctypes.byref(seqs()), lens,
+    assert lib.pa_decode_split_info(ctypes.byref(pool(block_size=24)), ctypes.byref(seqs()), lens,
                                     8, 0, ctypes.byref(info)) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_decode_split_info(ctypes.byref(pool()), ctypes.byref(seqs()), lens, 8, 24,
                                     ctypes.byref(info)) == pa.PA_ERR_INVALID_ARG
@@ -255,7 +257,7 @@ def test_noalloc_rejects_bad_arguments(lib):
     def call(p, s, q=FAKE, out=FAKE, hq=8, scale=0.1, part=0):
         return lib.pa_decode_noalloc(ctypes.byref(p), ctypes.byref(s), q, out, hq, scale, part,
                                      None)
-    assert call(pool(block_size=32), seqs()) == pa.PA_ERR_UNSUPPORTED
+    assert call(pool(block_size=24), seqs()) == pa.PA_ERR_UNSUPPORTED
     assert call(pool(), seqs(), hq=5) == pa.PA_ERR_INVALID_ARG
     assert call(pool(), seqs(), part=24) == pa.PA_ERR_INVALID_ARG
     assert call(pool(), seqs(), q=0) == pa.PA_ERR_INVALID_ARG
