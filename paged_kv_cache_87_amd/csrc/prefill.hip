@@ -17,8 +17,8 @@
 //   staged in LDS as [key][d] rows, double-buffered: at the start of a tile
 //   the next tile's K/V (loaded during the previous tile) are stashed and
 //   the loads of the tile after that are issued, so every load has a whole
-//   tile of math to arrive.  32-key tiles keep the kernel at 154 VGPRs and
-//   37 KB of LDS, so three workgroups (three waves per SIMD) share a CU; with
+//   tile of math to arrive.  32-key tiles keep the kernel at 164 VGPRs and
+//   39 KB of LDS, so three workgroups (three waves per SIMD) share a CU; with
 //   64-key tiles it needed 198 VGPRs and 70 KB, two per CU, and ran ~6 %
 //   slower.
 //
@@ -53,10 +53,13 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kCols = 128;            // (head, token) columns per workgroup
 constexpr int kKeys = 32;             // keys per K/V tile (2 blocks)
 constexpr int kHalves = kKeys / 32;   // 32-key halves per tile = loader passes
-// LDS row strides of K and V (bf16 elements): at head_dim 128, 68 and 72 dwords,
-// the second conflict-free for the transposing reads
+// LDS row strides of K and V (bf16 elements), for gfx950's 64 banks of 4 bytes:
+// a K fragment read (16 bytes per lane) serves 16 key rows at a time, which a
+// stride of D/2 + 4 dwords spreads over all 64 banks; a transposing V read (8
+// bytes per lane) serves 4 key rows x 64 bytes at a time, which need rows 16
+// banks apart: D/2 + 16 dwords (80 at head_dim 128, 48 at 64)
 template <int D> constexpr int kKStride = D + 8;
-template <int D> constexpr int kVStride = D + 16;
+template <int D> constexpr int kVStride = D + 32;
 constexpr float kPNegBig = -1.0e30f;
 constexpr float kPRescale = 8.f;
 
