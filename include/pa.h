@@ -442,6 +442,25 @@ pa_status pa_prefill(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void
                      int32_t max_q_len, int32_t num_q_heads, float scale,
                      hipStream_t stream);
 
+/*
+ * pa_read_checksum -- a plain read stream over a device buffer, to measure
+ * the read bandwidth a read-once kernel such as pa_decode can reach on this
+ * device (the decode's roofline is quoted against the HBM peak; this is the
+ * practical ceiling beside it).  Not part of the attention path.
+ *
+ *   buf        device, 16-byte aligned, `bytes` bytes (a multiple of 16).
+ *   words      device, [num_words] uint32 output; 1 <= num_words <= 65535.
+ *              Word i is the XOR of the little-endian 32-bit words of the
+ *              byte range [i*S, min((i+1)*S, bytes)), S = 16 * ceil(bytes /
+ *              16 / num_words); a word whose range is empty is 0.
+ * Every byte is read once with non-temporal 16-byte loads, one workgroup per
+ * output word.  PA_ERR_INVALID_ARG for a null pointer, bytes not a multiple
+ * of 16 or num_words out of range; PA_ERR_UNSUPPORTED if S exceeds 2 GiB.
+ * bytes == 0 writes zeros to every word.
+ */
+pa_status pa_read_checksum(const void* buf, size_t bytes, uint32_t* words, int32_t num_words,
+                           hipStream_t stream);
+
 /* Static text naming a status code. */
 const char* pa_status_string(int32_t status);
 

@@ -41,6 +41,7 @@ EXPORTED = (
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
     "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks", "pa_append_kv",
     "pa_decode_split_info", "pa_decode_noalloc", "pa_decode_noalloc_max_bytes",
+    "pa_read_checksum",
 )
 
 
@@ -120,6 +121,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_decode_split_info": (i32, [pool_p, seq_p, vp, i32, i32, ctypes.POINTER(PaDecodeSplit)]),
         "pa_decode_noalloc": (i32, [pool_p, seq_p, vp, vp, i32, f32, i32, vp]),
         "pa_decode_noalloc_max_bytes": (sz, []),
+        "pa_read_checksum": (i32, [vp, sz, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -596,6 +598,17 @@ def pa_swap_blocks(pool: KVPool, host_k: torch.Tensor, host_v: torch.Tensor,
     _check("pa_swap_blocks", st)
 
 
+def pa_read_checksum(buf: torch.Tensor, words: torch.Tensor, stream=None) -> None:
+    """The read-bandwidth probe: words[i] = XOR of the 32-bit words of share i
+    of ``buf``'s bytes (include/pa.h, pa_read_checksum)."""
+    if words.dim() != 1:
+        raise ValueError("words must be 1-D")
+    nbytes = buf.numel() * buf.element_size()
+    st = load_library().pa_read_checksum(_dev(buf, "buf"), nbytes, _dev(words, "words", torch.int32),
+                                         int(words.shape[0]), _stream(stream))
+    _check("pa_read_checksum", st)
+
+
 def pa_version() -> int:
     return int(load_library().pa_version())
 
@@ -604,7 +617,7 @@ __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
     "decode_workspace", "pa_decode", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit",
-    "pa_decode_noalloc", "BlockAllocator", "pa_copy_blocks",
+    "pa_decode_noalloc", "BlockAllocator", "pa_copy_blocks", "pa_read_checksum",
     "host_pool_c", "pa_swap_blocks", "paged_attention", "pa_append_kv", "check_tables", "check_slots",
     "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",
     "PA_LAYOUT_HEAD_MAJOR", "LAYOUTS",

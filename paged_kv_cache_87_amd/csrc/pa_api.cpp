@@ -358,6 +358,24 @@ pa_status pa_swap_blocks(const pa_kv_pool* device_pool, const pa_kv_pool* host_p
   return hip_status(pa::launch_copy_blocks(a, stream), "swap_blocks launch");
 }
 
+pa_status pa_read_checksum(const void* buf, size_t bytes, uint32_t* words, int32_t num_words,
+                           hipStream_t stream) {
+  clear_error();
+  if (buf == nullptr || words == nullptr) return fail(PA_ERR_INVALID_ARG, "buf or words is null");
+  if (bytes % 16 != 0) return fail(PA_ERR_INVALID_ARG, "bytes %zu is not a multiple of 16", bytes);
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "buf is not 16-byte aligned");
+  if (num_words < 1 || num_words > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_words %d (1 .. 65535)", num_words);
+  const uint64_t chunks = bytes / 16;
+  const uint64_t per = (chunks + num_words - 1) / num_words;
+  if (per > (uint64_t{1} << 27))
+    return fail(PA_ERR_UNSUPPORTED, "%llu bytes per word (at most 2 GiB)",
+                static_cast<unsigned long long>(per * 16));
+  pa::ReadChecksumArgs a{buf, chunks, per, words};
+  return hip_status(pa::launch_read_checksum(a, num_words, stream), "read_checksum launch");
+}
+
 size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs,
                                  int32_t num_q_heads, int32_t partition_size) {
   if (pool == nullptr || seqs == nullptr || seqs->num_seqs < 0 ||

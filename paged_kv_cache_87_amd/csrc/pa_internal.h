@@ -103,6 +103,14 @@ struct CopyBlocksArgs {
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
+struct ReadChecksumArgs {
+  const void* buf;            // device buffer, 16-byte aligned
+  uint64_t chunks;            // its 16-byte chunks
+  uint64_t chunks_per_word;   // chunks XORed into one output word (the last share may be shorter)
+  uint32_t* words;            // [num_words] device output
+};
+hipError_t launch_read_checksum(const ReadChecksumArgs& a, int num_words, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   void* out;

@@ -264,3 +264,15 @@ def test_noalloc_rejects_bad_arguments(lib):
     assert call(pool(), seqs(num_seqs=5000)) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_last_error() != b""
     assert lib.pa_decode_noalloc_max_bytes() == (256 + 16 * 1024 + 256) * 1024
+
+
+def test_read_checksum_rejects_bad_arguments(lib):
+    words = FAKE
+    assert lib.pa_read_checksum(None, 64, words, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE, 64, None, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE, 65, words, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE + 8, 64, words, 4, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE, 64, words, 0, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE, 64, words, 65536, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_read_checksum(FAKE, (2 << 30) + 16, words, 1, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_last_error() != b""
