@@ -76,7 +76,7 @@ template <int D>
 struct alignas(16) PrefillSmem {
   uint16_t k[2][kKeys][kKStride<D>];  // K tile, [key][d]
   uint16_t v[2][kKeys][kVStride<D>];  // V tile, [key][d]
-  int bad[2][4 * kHalves];            // per 8-key group of a tile: its table entry is not a block
+  uint32_t bad[2];                    // byte w: wave w's 8-key group of the tile is not in the pool
 };
 
 // The q / out rows of sequence s: [q0, q0 + q_len), q_start_loc clamped to
@@ -227,8 +227,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // descriptor; keys past the context read as zeros (offset past the
   // descriptor's size), so no pool row outside the context reaches the P.V.
   // A table entry that is not a block of the pool loads zeros too, and the
-  // first wave of each 16-key block records it (`bad`) so that its keys get
-  // no weight, as the decode skips such blocks
+  // wave records it in its byte of the tile's flag word (`bad`) so that those
+  // keys get no weight, as the decode skips such blocks.  Only a tile that
+  // reaches past the context needs the per-lane past-the-end offsets.
   const int ld_key = 8 * wave + kEPW * (lane / kCPR);   // first of the lane's keys
   const int ld_dc = lane % kCPR;                         // 8-element chunk of d
   // offset of the lane's first key and chunk from the wave's first key (the
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < kEPW; ++e) {
         const int kpos = kt * kKeys + ld_key + 32 * ps + e;
-        const uint32_t off = kpos < L ? ld_off + e * row_bytes : size;
+        const bool whole = kt * kKeys + kKeys <= L;       // the tile lies inside the context
+        const uint32_t off = (whole || kpos < L) ? ld_off + e * row_bytes : size;
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
         const u32x4 kx = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         const u32x4 vx = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
@@ -271,17 +273,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  uint16_t* const kst = &sm.k[0][ld_key][ld_dc * 8];
+  uint16_t* const vst = &sm.v[0][ld_key][ld_dc * 8];
   auto stash = [&](int buf) {
 #pragma unroll
     for (int ps = 0; ps < kHalves; ++ps) {
 #pragma unroll
       for (int e = 0; e < kEPW; ++e) {
-        const int key = ld_key + 32 * ps + e;
-        *reinterpret_cast<uint4*>(&sm.k[buf][key][ld_dc * 8]) = kreg[ps][e];
-        *reinterpret_cast<uint4*>(&sm.v[buf][key][ld_dc * 8]) = vreg[ps][e];
+        const int r = 32 * ps + e;
+        *reinterpret_cast<uint4*>(kst + buf * (kKeys * kKStride<kD>) + r * kKStride<kD>) = kreg[ps][e];
+        *reinterpret_cast<uint4*>(vst + buf * (kKeys * kVStride<kD>) + r * kVStride<kD>) = vreg[ps][e];
       }
-      // wave w loads the tile's keys 8 w .. 8 w + 7
-      if (lane == 0) sm.bad[buf][wave + 4 * ps] = kbad[ps];
+      // wave w loads the tile's keys 8 w .. 8 w + 7: byte w of the tile's flag word
+      reinterpret_cast<uint8_t*>(&sm.bad[buf])[wave] = static_cast<uint8_t>(kbad[ps]);
     }
   };
   // transposing-read source address of this lane: key row 4 * half + (lane % 16) / 4,
@@ -352,14 +356,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
           if (8 * (r >> 2) + (r & 3) > lim) st[t][r] = -INFINITY;
       }
       // keys of a block whose table entry is not in the pool get no weight
-      const int4 bad = *reinterpret_cast<const int4*>(&sm.bad[buf][4 * t]);
-      if (bad.x | bad.y | bad.z | bad.w) {
+      const uint32_t bad = static_cast<uint32_t>(uniform(static_cast<int>(sm.bad[buf])));
+      if (bad) {
         // accumulator entry r holds a key of the group r / 4
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int b = (r >> 2) == 0 ? bad.x : (r >> 2) == 1 ? bad.y : (r >> 2) == 2 ? bad.z : bad.w;
-          if (b) st[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if ((bad >> (8 * (r >> 2))) & 0xffu) st[t][r] = -INFINITY;
       }
       float tmax = st[t][0];
 #pragma unroll
