@@ -448,8 +448,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct alignas(16) PrefillSmemF32 {
-  float k[2][kKeys][D + 4];           // K tile, [key][d]; rows 16 bytes apart mod 128
-  float v[2][kKeys][D + 4];           // V tile, [key][d]
+  // K rows D + 4 floats apart: a 16-byte fragment read serves 16 key rows at
+  // a time, 4 banks apart over all 64.  V rows D + 8 apart: a V read (one
+  // float a lane) serves the two keys 4 rows apart of the lane halves, 32
+  // consecutive floats each, which then fall in opposite halves of the banks.
+  float k[2][kKeys][D + 4];           // K tile, [key][d]
+  float v[2][kKeys][D + 8];           // V tile, [key][d]
   int bad[2][4 * kHalves];
 };
 
