@@ -336,24 +336,28 @@ size_t pa_decode_workspace_bytes(const pa_kv_pool* pool, const pa_seq_desc* seqs
  * partition_size: 0 (or at least the longest context) = each (sequence, KV
  * head) pair in one pass.  Otherwise a multiple of 16 that turns on
  * the split-context decode: the blocks of all pairs, laid end to end, are cut
- * into equal slices of at least partition_size tokens, one per workgroup that
- * the GPU holds at once, so every workgroup reads the same number of bytes
- * whatever the mix of context lengths.  A pair cut by slice boundaries is
- * computed in pieces, each keeping its own maximum, sum and normalised
- * output, and the workgroup that finishes its last piece merges them by
- * log-sum-exp weighting, in the same kernel.
+ * into slices of at least partition_size tokens, one per workgroup that the
+ * GPU holds at once.  When the non-empty contexts differ in length the
+ * slices cover nine tenths of the work and the rest is cut into chunks of a
+ * sixteenth of a slice (at least partition_size tokens) that the workgroups
+ * take one at a time as they finish, so faster workgroups take more; with
+ * equal lengths the slices cover it all.  A pair cut by slice or chunk
+ * boundaries is computed in pieces, each keeping its own maximum, sum and
+ * normalised output, and the workgroup that finishes its last piece merges
+ * them by log-sum-exp weighting, in token order, in the same kernel.
  *
  * workspace (device, 256-byte aligned, at least pa_decode_workspace_bytes(...)
  * bytes; may be NULL when that is 0): its first 256 KiB hold one arrival
- * counter per (sequence, KV head), the rest the pieces' results.  The
- * counters must be zero before the first call that uses the workspace (zero
- * the whole buffer once when allocating it); every call leaves them zero
- * again, so one workspace serves any later batch shape.  The rest's contents
+ * counter per (sequence, KV head) and, in their last 256 bytes, the
+ * counters that hand out the chunks; the rest holds the pieces' results.
+ * The counters must be zero before the first call that uses the workspace
+ * (zero the whole buffer once when allocating it); every call leaves them
+ * zero again, so one workspace serves any later batch shape.  The rest's contents
  * on entry do not matter.  Calls that share a workspace must not overlap.
  *
  * Supported: num_q_heads / num_kv_heads in {1, 2, 4, 8}; num_seqs <= 4096;
  * num_kv_heads * num_seqs * ceil(max_context_len / 16) < 2^31; split,
- * num_seqs * num_kv_heads <= 65536.
+ * num_seqs * num_kv_heads <= 65472.
  */
 pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* q,
                     void* out, int32_t num_q_heads, float scale, int32_t partition_size,
@@ -393,19 +397,22 @@ size_t pa_decode_noalloc_max_bytes(void);
  * host_context_lens (host, int32 [num_seqs]) is a host copy of
  * seqs->context_lens; the other arguments are those of pa_decode (q, out and
  * the workspace are not needed).  Fills *info: the workgroups of the launch;
- * slice_blocks, the work each workgroup takes in blocks (each segment of a
+ * slice_blocks, each workgroup's static slice in blocks (each segment of a
  * (sequence, KV head) pair priced as a fixed number of extra blocks), 0 when
- * the context is not split; and how many pieces the non-empty pairs are cut
- * into (1 each when not split).  partition_size is a lower bound of the
- * slice, not the slice itself: the slice is the larger of partition_size / 16
- * blocks and the batch's work divided by the workgroups.
+ * the context is not split; chunk_blocks and units, the chunks handed out
+ * after the slices (0 when none) and the slices and chunks in all; and how
+ * many pieces the non-empty pairs are cut into (1 each when not split).
+ * partition_size is a lower bound of the slice and the chunk, not the
+ * slice itself.
  */
 typedef struct pa_decode_split {
   int32_t workgroups;
-  int32_t slice_blocks;
-  int32_t pairs;        /* (sequence, KV head) pairs with a non-empty context */
-  int32_t max_pieces;   /* most pieces of one pair */
-  float mean_pieces;    /* mean pieces per pair */
+  int32_t slice_blocks;  /* each workgroup's static slice */
+  int32_t pairs;         /* (sequence, KV head) pairs with a non-empty context */
+  int32_t max_pieces;    /* most pieces of one pair */
+  float mean_pieces;     /* mean pieces per pair */
+  int32_t chunk_blocks;  /* the chunks handed out after the slices (0: none) */
+  int32_t units;         /* slices + chunks */
 } pa_decode_split;
 
 pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,

@@ -76,6 +76,8 @@ class PaDecodeSplit(ctypes.Structure):
         ("pairs", ctypes.c_int32),
         ("max_pieces", ctypes.c_int32),
         ("mean_pieces", ctypes.c_float),
+        ("chunk_blocks", ctypes.c_int32),
+        ("units", ctypes.c_int32),
     ]
 
 
@@ -400,9 +402,10 @@ def pa_decode_workspace_bytes(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
 
 def pa_decode_split_info(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
                          partition_size: int) -> dict:
-    """How pa_decode splits this batch: workgroups, slice length in blocks
-    (0 = not split) and pieces per (sequence, KV head) pair.  Reads a host
-    copy of the context lengths."""
+    """How pa_decode splits this batch: workgroups, static slice length in
+    blocks (0 = not split), the chunks handed out after the slices (length,
+    0 = none; slices + chunks = units) and pieces per (sequence, KV head)
+    pair.  Reads a host copy of the context lengths."""
     lens = np.ascontiguousarray(seqs.context_lens.cpu().numpy(), dtype=np.int32)
     info = PaDecodeSplit()
     cp, cs = pool.c(), seqs.c()
@@ -411,6 +414,7 @@ def pa_decode_split_info(pool: KVPool, seqs: SeqDesc, num_q_heads: int,
                                              int(partition_size), ctypes.byref(info))
     _check("pa_decode_split_info", st)
     return {"workgroups": info.workgroups, "slice_blocks": info.slice_blocks,
+            "chunk_blocks": info.chunk_blocks, "units": info.units,
             "pairs": info.pairs, "max_pieces": info.max_pieces,
             "mean_pieces": float(info.mean_pieces)}
 

@@ -191,21 +191,22 @@ __device__ __forceinline__ float load_shared(const float* p) {
 // "Online Softmax": the same max/sum rescaling that joins two blocks joins
 // two pieces), taken in token order with a running maximum.  The pair's
 // blocks sit at work positions [A, E) and its work range starts at A0 <= A;
-// its piece in slice i sits in partial slot 2i, or 2i + 1 for the first
-// slice when that slice starts before the pair's work range (then an
-// earlier pair's segment came first in it).  Each thread owns E_
+// its piece in unit i (a static slice or a chunk, numbered in position order)
+// sits in partial slot 2i, or 2i + 1 for the first unit when that unit starts
+// before the pair's work range (then an earlier pair's segment came first in
+// it).  Each thread owns E_
 // output elements; the loads of eight pieces are issued together, so a merge
 // of up to eight pieces costs one memory round trip.
 constexpr int kMergeBatch = 8;
 
 template <typename T, int D, int N, int kThreads>
 __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, int A0, int A,
-                                           int E, int Q, int tid) {
+                                           int E, const UnitPlan& up, int tid) {
   constexpr int kOut = N * D;
   constexpr int E_ = (kOut + kThreads - 1) / kThreads;
-  const int ia = A / Q;
-  const int n = (E - 1) / Q - ia + 1;
-  const bool first_tail = ia * Q < A0;
+  const int ia = up.of(A);
+  const int n = up.of(E - 1) - ia + 1;
+  const bool first_tail = up.start(ia) < A0;
   float M[E_], wsum[E_], osum[E_];
   int hd[E_], dd[E_];
 #pragma unroll
@@ -266,17 +267,22 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 // ranges lie end to end at W_p = Hkv * pre_s + g * c_s, B in all; block j
 // of the pair sits at W_p + seg_cost + j.
 //
-// Split (min_slice_blocks > 0): the work range is cut into slices of
-// Q = max(ceil(B / grid), min_slice_blocks) and workgroup i takes slice i,
-// so every workgroup gets the same work whatever the mix of context
-// lengths.  The part of a pair inside a slice (a segment: the pair's blocks
-// whose positions fall in the slice) keeps its own online-softmax state.  Only the first and the last segment
-// of a slice can be pieces of a pair that goes on in another slice; they
-// write (o, m, l) to partial slots 2i and 2i + 1, the segments between them
-// are whole pairs and write `out`.  At the end of its slice a workgroup
-// counts its pieces at their pairs' arrival counters, and the last arrival
-// of a pair merges it.  Without a split, workgroup i takes pairs i,
-// i + grid, ... whole.
+// Split (min_slice_blocks > 0): the work range is cut into units (unit_plan):
+// one static slice per workgroup, workgroup i taking slice i, so every
+// workgroup gets the same work whatever the mix of context lengths; when the
+// non-empty pairs differ in length the slices cover nine tenths of it and
+// the rest is cut into chunks that the workgroups take from a counter as
+// they finish, so the ones that run slower (their speed differs by die and
+// by CU, from call to call alike) take fewer.  The part of a pair inside a
+// unit (a segment: the pair's blocks whose positions fall in the unit) keeps
+// its own online-softmax state.  Only the first and the last segment of a
+// unit can be pieces of a pair that goes on in another unit; they write
+// (o, m, l) to partial slots 2u and 2u + 1, the segments between them are
+// whole pairs and write `out`.  At the end of a unit its workgroup counts
+// its pieces at their pairs' arrival counters, and the last arrival of a
+// pair merges it.  Which workgroup computes a unit does not change what it
+// computes, so the result is the same bit for bit from call to call.
+// Without a split, workgroup i takes pairs i, i + grid, ... whole.
 //
 // Inside a segment the waves take its blocks round-robin, each through
 // a ring of kRing register buffers (kRing-1 blocks in flight while one is
@@ -307,6 +313,8 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   __shared__ float sm_m[kWaves][N];
   __shared__ float sm_l[kWaves][N];
   __shared__ int sm_last[2];
+  __shared__ int sm_nb[kWaves][2];   // per wave: least and most blocks of a non-empty pair
+  __shared__ int sm_unit;
 
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
@@ -324,11 +332,26 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     const int b0 = min(S, tid * per);
     const int b1 = min(S, b0 + per);
     int cb = 0;
+    int nb_lo = 0x7fffffff, nb_hi = 0;
     for (int q = b0; q < b1; ++q) {
       int L = a.context_lens[q];
       L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
       sm_ctx[q] = L;
-      cb += L > 0 ? (L + kUnit - 1) / kUnit + a.seg_cost : 0;
+      const int nbq = (L + kUnit - 1) / kUnit;
+      cb += L > 0 ? nbq + a.seg_cost : 0;
+      if (L > 0) {
+        nb_lo = min(nb_lo, nbq);
+        nb_hi = max(nb_hi, nbq);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      nb_lo = min(nb_lo, __shfl_xor(nb_lo, off));
+      nb_hi = max(nb_hi, __shfl_xor(nb_hi, off));
+    }
+    if (lane == 0) {
+      sm_nb[wave][0] = nb_lo;
+      sm_nb[wave][1] = nb_hi;
     }
     sm_scan[tid] = cb;
     __syncthreads();
@@ -374,14 +397,19 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   const bool split = a.min_slice_blocks > 0;
   const int n_pairs = S * Hkv;
   const int B = Hkv * sm_pre[S];               // the host keeps this below 2^31
-  int Q = 1, F0 = 0, F1 = 0;                   // this workgroup's slice [F0, F1)
+  UnitPlan up{};                               // split: static slices, then handed-out chunks
   if (split) {
-    Q = max((B + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x),
-            a.min_slice_blocks);
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * Q;
-    F0 = static_cast<int>(f0 < B ? f0 : B);
-    F1 = static_cast<int>(f0 + Q < B ? f0 + Q : B);
+    int nb_lo = 0x7fffffff, nb_hi = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      nb_lo = min(nb_lo, sm_nb[w][0]);
+      nb_hi = max(nb_hi, sm_nb[w][1]);
+    }
+    up = unit_plan(B, static_cast<int>(gridDim.x), a.min_slice_blocks, a.max_slices,
+                   nb_lo >= nb_hi);
   }
+  int u = blockIdx.x;                          // split: the unit being walked
+  int F0 = 0, F1 = 0;                          // its work range [F0, F1)
   const int C = a.seg_cost;
   auto nb_of = [&](int q) { return (sm_ctx[q] + kUnit - 1) / kUnit; };
   auto cost_of = [&](int q) { return sm_pre[q + 1] - sm_pre[q]; };
@@ -413,7 +441,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       x.blk1 = min(nb, F1 - first_blk);
       x.end = first_blk + x.blk1;
       x.slot = (x.blk0 == 0 && x.blk1 == nb) ? -1
-             : 2 * static_cast<int>(blockIdx.x) + (pos == F0 ? 0 : 1);
+             : 2 * u + (pos == F0 ? 0 : 1);
     } else {
       x.s = pos / Hkv;
       x.g = pos - x.s * Hkv;
@@ -432,7 +460,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   auto next_pos = [&](const Seg& x, int pos) {
     return split ? x.end : skip_empty(pos + gridDim.x);
   };
-  const int pos_end = split ? F1 : n_pairs;
+  int pos_end = n_pairs;
   // lane t: table entries of this wave's t-th 16-token unit of the chunk at
   // c0.  Unit j holds positions 16 j .. 16 j + 15: with blocks of 16 tokens
   // or more, the rows 16 j mod B .. of block 16 j / B; with blocks of 8, two
@@ -477,378 +505,411 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   const char* vpool = static_cast<const char*>(a.v_cache);
   const float sl2 = a.scale_log2;
 
-  // ---- current segment state ----------------------------------------------------
-  int pos = split ? F0 : skip_empty(blockIdx.x);
-  if (pos >= pos_end) return;
-  Seg cur = seg_at(pos);
-  if (cur.blk1 <= cur.blk0) return;  // the slice holds no block
-  int c0 = cur.blk0;                 // first block of the current chunk
-  int nk = 0;                        // this wave's blocks in the current chunk
-  int2 tbl = load_tbl(cur, c0);
-  uint32_t qv[N][NW];
-  load_q(cur, qv);
-  uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
-  auto chunk_blocks = [&](const Seg& x, int cs) {
-    const int ce = min(x.blk1, cs + kChunkBlocks);
-    return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
-  };
-
-  // pieces of pairs stored by this slice: its first segment (slot 2i) and its
-  // last (slot 2i + 1), counted at the end
-  int pa_s = -1, pa_g = 0, pb_s = -1, pb_g = 0;
-
-  float m = kNegBig, l = 0.f;
-  float acc[N][EPL];
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-
-  // Issue the loads of this wave's k-th unit of the current chunk into
-  // (kf, vf) and return the mask of its valid tokens (bit t: token 16 j + t).
-  // Past the wave's last unit, or for a table entry outside the pool, the
-  // descriptors have size 0: the loads return zeros without touching memory
-  // and the tokens of that block count as invalid.  Token rows 0 .. 7 of the
-  // unit (uu = 0, 1) come through the first descriptor, rows 8 .. 15 through
-  // the second, which is the first one again unless blocks hold 8 tokens.
-  auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
-    int phys = -1, phys2 = -1;
-    int nvalid = 0;
-    int sub = 0;                     // first token row of the unit inside its block
-    if (k < nk) {
-      const int j = c0 + wave + kWaves * k;
-      phys = __builtin_amdgcn_readlane(tbl.x, k);
-      phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
-      const int n = cur.tok1 - j * kUnit;
-      nvalid = n < kUnit ? n : kUnit;
-      sub = small ? 0 : (j << 4) & ((1 << bshift) - 1);
-    }
-    const bool ok = phys >= 0 && phys < a.num_blocks;
-    const bool ok2 = phys2 >= 0 && phys2 < a.num_blocks;
-    const int vmask = ((ok ? 0x00ff : 0) | (ok2 ? 0xff00 : 0)) & ((1 << nvalid) - 1);
-    const uint32_t sub_bytes = static_cast<uint32_t>(sub) * row_bytes;
-    const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride + sub_bytes : 0;
-    const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
-    const Rsrc rk = make_rsrc(kpool + off, size);
-    const Rsrc rv = make_rsrc(vpool + off, size);
-    const int64_t off2 = ok2 ? static_cast<int64_t>(phys2) * block_stride : 0;
-    const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
-    const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
-    const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
-#pragma unroll
-    for (int uu = 2; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
-#pragma unroll
-    for (int uu = 2; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
-    return vmask;
-  };
-
-  // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
-  // running max and sum, then P.V.  The reference max of a stream only moves
-  // when a score passes it by more than kRescaleLog2 (then the accumulators
-  // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
-  // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
-  auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
-    float z[4];
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) {
-      float part_dot[N];
-#pragma unroll
-      for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
-      z[uu] = reduce_scatter<R>(part_dot) * sl2;
-    }
-    // tokens past the context (partial last unit, or a unit the ring runs
-    // past its end) or in a block outside the pool get no weight and a zero
-    // value row, whatever the pool holds there
-    if (vmask != 0xffff) {
-#pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        if (((vmask >> (row + 4 * uu)) & 1) == 0) {
-          z[uu] = -INFINITY;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
-        }
-      }
-    }
-    const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
-      const float m_new = mx > m + kRescaleLog2 ? mx : m;
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
-      float alpha_j[N];
-      bcast_all<R>(alpha, alpha_j);
-#pragma unroll
-      for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
-    }
-    float p[4];
-#pragma unroll
-    for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
-
-    if constexpr (sizeof(T) == 2) {
-      // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
-      // with one v_dot2_f32_bf16 per (head, element): the value rows of the
-      // pair are interleaved with v_perm, the weights packed to bf16.  The
-      // running sum adds the same rounded weights (slot 0 is the lane's own
-      // head), so the normalised output is a convex combination of the V rows.
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int ua = 2 * pr, ub = 2 * pr + 1;
-        float pa[N], pb[N];
-        bcast_all<R>(p[ua], pa);
-        bcast_all<R>(p[ub], pb);
-        uint32_t pw[N];
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const f32x2 two = {pa[j], pb[j]};
-          pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
-        }
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[0]),
-                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), l, false);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          // element 2w: low halves of token a and b; element 2w+1: high halves
-          const uint32_t ve = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x05040100u);
-          const uint32_t vo = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x07060302u);
-#pragma unroll
-          for (int j = 0; j < N; ++j) {
-            acc[j][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, ve), acc[j][2 * w],
-                false);
-            acc[j][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, vo),
-                acc[j][2 * w + 1], false);
-          }
-        }
-      }
-    } else {
-      l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        float pj[N];
-        bcast_all<R>(p[uu], pj);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float v = frag_elem<T, D>(vf[uu], e);
-#pragma unroll
-          for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
-        }
-      }
-    }
-  };
-
-  // ---- prologue: the first segment's table and query rows, then the next one's
-  // (left in flight), then the first segment's primed ring blocks --------------
-  __builtin_amdgcn_s_waitcnt(0);
-  int pos_n = next_pos(cur, pos);
-  bool has_next = pos_n < pos_end;
-  Seg nxt = has_next ? seg_at(pos_n) : cur;
-  has_next = has_next && nxt.blk1 > nxt.blk0;
-  int2 tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
-  nk = chunk_blocks(cur, c0);
-
-  F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
-  int n0 = issue(0, k0, v0);
-  __builtin_amdgcn_sched_barrier(0);
-  int n1 = 0;
-  if constexpr (kRing == 3) n1 = issue(1, k1, v1);
-  __builtin_amdgcn_sched_barrier(0);
-  int n2 = 0;
-
+  // ---- units: the slice of this workgroup, then chunks handed out (split);
+  // without a split, the workgroup's whole pairs --------------------------------
+  int* const ctl = a.counters + kPairSlots;   // [0] units handed out, [1] workgroups done
   for (;;) {
-    // ---- the ring over this chunk of the current segment (one exit, at the
-    // bottom: a trip always runs every stage; stages past the wave's last
-    // block see size-0 descriptors and zero valid tokens and change nothing)
-    if constexpr (kRing == 2) {
-      for (int k = 0; k < nk; k += 2) {
-        n1 = issue(k + 1, k1, v1);
-        __builtin_amdgcn_sched_barrier(0);
-        process(k0, v0, n0);
-        n0 = issue(k + 2, k0, v0);
-        __builtin_amdgcn_sched_barrier(0);
-        process(k1, v1, n1);
-      }
-    } else {
-      for (int k = 0; k < nk; k += 3) {
-        n2 = issue(k + 2, k2, v2);
-        __builtin_amdgcn_sched_barrier(0);
-        process(k0, v0, n0);
-        n0 = issue(k + 3, k0, v0);
-        __builtin_amdgcn_sched_barrier(0);
-        process(k1, v1, n1);
-        n1 = issue(k + 4, k1, v1);
-        __builtin_amdgcn_sched_barrier(0);
-        process(k2, v2, n2);
-      }
+    if (split) {
+      F0 = up.start(u);
+      F1 = up.end(u);
+      pos_end = F1;
     }
+    // pieces of pairs stored by this unit: its first segment (slot 2u) and its
+    // last (slot 2u + 1), counted at its end
+    int pa_s = -1, pa_g = 0, pb_s = -1, pb_g = 0;
+    int pos = split ? F0 : skip_empty(blockIdx.x);
+    Seg cur;
+    bool any = pos < pos_end;
+    if (any) {
+      cur = seg_at(pos);
+      any = cur.blk1 > cur.blk0;     // else the unit holds no block
+    }
+    if (any) {
+    int c0 = cur.blk0;                 // first block of the current chunk
+    int nk = 0;                        // this wave's blocks in the current chunk
+    int2 tbl = load_tbl(cur, c0);
+    uint32_t qv[N][NW];
+    load_q(cur, qv);
+    uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
+    auto chunk_blocks = [&](const Seg& x, int cs) {
+      const int ce = min(x.blk1, cs + kChunkBlocks);
+      return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
+    };
 
-    // ---- a segment longer than one chunk: next chunk of the same segment -----
-    if (c0 + kChunkBlocks < cur.blk1) {
-      c0 += kChunkBlocks;
-      tbl = load_tbl(cur, c0);
-      __builtin_amdgcn_s_waitcnt(0);
-      nk = chunk_blocks(cur, c0);
-      n0 = issue(0, k0, v0);
-      __builtin_amdgcn_sched_barrier(0);
-      n1 = issue(1, k1, v1);
-      __builtin_amdgcn_sched_barrier(0);
-      continue;
-    }
+    float m = kNegBig, l = 0.f;
+    float acc[N][EPL];
+  #pragma unroll
+    for (int j = 0; j < N; ++j)
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
 
-    // ---- merge the four rows of each wave -------------------------------------
-    {
-      float ms[N], ls[N];
-      bcast_all<R>(m, ms);
-      bcast_all<R>(l, ls);
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const float mo = __shfl_xor(ms[j], off);
-          const float lo = __shfl_xor(ls[j], off);
-          const float mn = fmaxf(ms[j], mo);
-          const float ca = fast_exp2(ms[j] - mn);
-          const float cb = fast_exp2(mo - mn);
-          ls[j] = ls[j] * ca + lo * cb;
-          ms[j] = mn;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e)
-            acc[j][e] = acc[j][e] * ca + __shfl_xor(acc[j][e], off) * cb;
-        }
+    // Issue the loads of this wave's k-th unit of the current chunk into
+    // (kf, vf) and return the mask of its valid tokens (bit t: token 16 j + t).
+    // Past the wave's last unit, or for a table entry outside the pool, the
+    // descriptors have size 0: the loads return zeros without touching memory
+    // and the tokens of that block count as invalid.  Token rows 0 .. 7 of the
+    // unit (uu = 0, 1) come through the first descriptor, rows 8 .. 15 through
+    // the second, which is the first one again unless blocks hold 8 tokens.
+    auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
+      int phys = -1, phys2 = -1;
+      int nvalid = 0;
+      int sub = 0;                     // first token row of the unit inside its block
+      if (k < nk) {
+        const int j = c0 + wave + kWaves * k;
+        phys = __builtin_amdgcn_readlane(tbl.x, k);
+        phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
+        const int n = cur.tok1 - j * kUnit;
+        nvalid = n < kUnit ? n : kUnit;
+        sub = small ? 0 : (j << 4) & ((1 << bshift) - 1);
       }
-      // ---- merge the waves through LDS ------------------------------------------
-      if (row == 0) {
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
-        if ((li & (W - 1)) == 0) {
-          sm_m[wave][own] = ms[0];
-          sm_l[wave][own] = ls[0];
-        }
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      const bool ok2 = phys2 >= 0 && phys2 < a.num_blocks;
+      const int vmask = ((ok ? 0x00ff : 0) | (ok2 ? 0xff00 : 0)) & ((1 << nvalid) - 1);
+      const uint32_t sub_bytes = static_cast<uint32_t>(sub) * row_bytes;
+      const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride + sub_bytes : 0;
+      const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
+      const Rsrc rk = make_rsrc(kpool + off, size);
+      const Rsrc rv = make_rsrc(vpool + off, size);
+      const int64_t off2 = ok2 ? static_cast<int64_t>(phys2) * block_stride : 0;
+      const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
+      const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
+      const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
+  #pragma unroll
+      for (int uu = 0; uu < 2; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
+  #pragma unroll
+      for (int uu = 2; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
+  #pragma unroll
+      for (int uu = 0; uu < 2; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
+  #pragma unroll
+      for (int uu = 2; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
+      return vmask;
+    };
+
+    // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
+    // running max and sum, then P.V.  The reference max of a stream only moves
+    // when a score passes it by more than kRescaleLog2 (then the accumulators
+    // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
+    // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
+    auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
+      float z[4];
+  #pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        float part_dot[N];
+  #pragma unroll
+        for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
+        z[uu] = reduce_scatter<R>(part_dot) * sl2;
       }
-    }
-    __syncthreads();
-    {
-      const bool direct = cur.slot < 0;
-      for (int o = tid; o < N * D; o += kThreads) {
-        const int h = o / D;
-        const int d = o - h * D;
-        float M = sm_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-        float lsum = 0.f, osum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float c = fast_exp2(sm_m[w][h] - M);
-          lsum += sm_l[w][h] * c;
-          osum += sm_acc[w][h][d] * c;
-        }
-        const float val = lsum > 0.f ? osum / lsum : 0.f;
-        const int qh = cur.g * N + h;
-        if (direct) {
-          store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
-        } else {
-          const int64_t pi = static_cast<int64_t>(cur.slot) * N + h;
-          store_shared(a.part_o + pi * D + d, val);
-          if (d == 0) {
-            store_shared(a.part_ml + pi * 2 + 0, M);
-            store_shared(a.part_ml + pi * 2 + 1, lsum);
+      // tokens past the context (partial last unit, or a unit the ring runs
+      // past its end) or in a block outside the pool get no weight and a zero
+      // value row, whatever the pool holds there
+      if (vmask != 0xffff) {
+  #pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          if (((vmask >> (row + 4 * uu)) & 1) == 0) {
+            z[uu] = -INFINITY;
+  #pragma unroll
+            for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
           }
         }
       }
-    }
-    __syncthreads();   // LDS merge buffers are reused by the next segment
-    if (cur.slot >= 0) {
-      if (cur.slot & 1) { pb_s = cur.s; pb_g = cur.g; }
-      else { pa_s = cur.s; pa_g = cur.g; }
-    }
-    if (!has_next) break;
+      const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
+        const float m_new = mx > m + kRescaleLog2 ? mx : m;
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        l *= alpha;
+        float alpha_j[N];
+        bcast_all<R>(alpha, alpha_j);
+  #pragma unroll
+        for (int j = 0; j < N; ++j)
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
+      }
+      float p[4];
+  #pragma unroll
+      for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
 
-    // ---- move on: loads of the segment after next, then the next segment's
-    // primed ring blocks (in that order, so the primed blocks are the
-    // youngest loads)
-    cur = nxt;
-    pos = pos_n;
-    pos_n = next_pos(cur, pos);
-    has_next = pos_n < pos_end;
-    if (has_next) {
-      nxt = seg_at(pos_n);
-      has_next = nxt.blk1 > nxt.blk0;
-    }
-    tbl = tbl_nxt;
-    load_q(cur, qv);
-    tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
-    c0 = cur.blk0;
+      if constexpr (sizeof(T) == 2) {
+        // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
+        // with one v_dot2_f32_bf16 per (head, element): the value rows of the
+        // pair are interleaved with v_perm, the weights packed to bf16.  The
+        // running sum adds the same rounded weights (slot 0 is the lane's own
+        // head), so the normalised output is a convex combination of the V rows.
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+  #pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int ua = 2 * pr, ub = 2 * pr + 1;
+          float pa[N], pb[N];
+          bcast_all<R>(p[ua], pa);
+          bcast_all<R>(p[ub], pb);
+          uint32_t pw[N];
+  #pragma unroll
+          for (int j = 0; j < N; ++j) {
+            const f32x2 two = {pa[j], pb[j]};
+            pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+          }
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[0]),
+                                              __builtin_bit_cast(bf16x2, 0x3f803f80u), l, false);
+  #pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            // element 2w: low halves of token a and b; element 2w+1: high halves
+            const uint32_t ve = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x05040100u);
+            const uint32_t vo = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x07060302u);
+  #pragma unroll
+            for (int j = 0; j < N; ++j) {
+              acc[j][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, ve), acc[j][2 * w],
+                  false);
+              acc[j][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                  __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, vo),
+                  acc[j][2 * w + 1], false);
+            }
+          }
+        }
+      } else {
+        l += (p[0] + p[1]) + (p[2] + p[3]);
+  #pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          float pj[N];
+          bcast_all<R>(p[uu], pj);
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const float v = frag_elem<T, D>(vf[uu], e);
+  #pragma unroll
+            for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
+          }
+        }
+      }
+    };
+
+    // ---- prologue: the first segment's table and query rows, then the next one's
+    // (left in flight), then the first segment's primed ring blocks --------------
+    __builtin_amdgcn_s_waitcnt(0);
+    int pos_n = next_pos(cur, pos);
+    bool has_next = pos_n < pos_end;
+    Seg nxt = has_next ? seg_at(pos_n) : cur;
+    has_next = has_next && nxt.blk1 > nxt.blk0;
+    int2 tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
     nk = chunk_blocks(cur, c0);
-    lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
-    m = kNegBig;
-    l = 0.f;
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-    n0 = issue(0, k0, v0);
+
+    F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+    int n0 = issue(0, k0, v0);
     __builtin_amdgcn_sched_barrier(0);
+    int n1 = 0;
     if constexpr (kRing == 3) n1 = issue(1, k1, v1);
     __builtin_amdgcn_sched_barrier(0);
-  }
+    int n2 = 0;
 
-  // ---- arrivals of this slice's pieces ------------------------------------------
-  // Publication: every wave waits until its piece stores (device-coherent
-  // atomic stores) are complete, then the workgroup barrier, then thread 0
-  // counts the pieces with an agent-scope add; the add therefore reaches
-  // memory after every piece store of the workgroup.  Acquisition: the
-  // workgroup whose add completes a pair runs an agent-scope acquire fence
-  // before the barrier that releases its threads to the merge, whose loads
-  // are device-coherent atomic loads.  The add itself is relaxed: an
-  // agent-scope release would add an L2 write-back (buffer_wbl2) per
-  // workgroup, which publishes plain stores this protocol does not use and
-  // cost 15 us a call on the 64-sequence random-length batch.  The last
-  // arrival of a pair merges its pieces and leaves the counter at zero for
-  // the next call.
-  if (pa_s >= 0 || pb_s >= 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // work position of the pair's block 0; its work range starts C earlier
-    auto pair_start = [&](int q, int g) { return Hkv * sm_pre[q] + g * cost_of(q) + C; };
-    auto pieces = [&](int q, int g) {
-      const int A = pair_start(q, g);
-      return (A + nb_of(q) - 1) / Q - A / Q + 1;
-    };
-    if (tid == 0) {
-      int last_a = 0, last_b = 0;
-      if (pa_s >= 0)
-        last_a = __hip_atomic_fetch_add(a.counters + pa_s * Hkv + pa_g, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == pieces(pa_s, pa_g) - 1;
-      if (pb_s >= 0)
-        last_b = __hip_atomic_fetch_add(a.counters + pb_s * Hkv + pb_g, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == pieces(pb_s, pb_g) - 1;
-      if (last_a | last_b) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      sm_last[0] = last_a;
-      sm_last[1] = last_b;
+    for (;;) {
+      // ---- the ring over this chunk of the current segment (one exit, at the
+      // bottom: a trip always runs every stage; stages past the wave's last
+      // block see size-0 descriptors and zero valid tokens and change nothing)
+      if constexpr (kRing == 2) {
+        for (int k = 0; k < nk; k += 2) {
+          n1 = issue(k + 1, k1, v1);
+          __builtin_amdgcn_sched_barrier(0);
+          process(k0, v0, n0);
+          n0 = issue(k + 2, k0, v0);
+          __builtin_amdgcn_sched_barrier(0);
+          process(k1, v1, n1);
+        }
+      } else {
+        for (int k = 0; k < nk; k += 3) {
+          n2 = issue(k + 2, k2, v2);
+          __builtin_amdgcn_sched_barrier(0);
+          process(k0, v0, n0);
+          n0 = issue(k + 3, k0, v0);
+          __builtin_amdgcn_sched_barrier(0);
+          process(k1, v1, n1);
+          n1 = issue(k + 4, k1, v1);
+          __builtin_amdgcn_sched_barrier(0);
+          process(k2, v2, n2);
+        }
+      }
+
+      // ---- a segment longer than one chunk: next chunk of the same segment -----
+      if (c0 + kChunkBlocks < cur.blk1) {
+        c0 += kChunkBlocks;
+        tbl = load_tbl(cur, c0);
+        __builtin_amdgcn_s_waitcnt(0);
+        nk = chunk_blocks(cur, c0);
+        n0 = issue(0, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        n1 = issue(1, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
+
+      // ---- merge the four rows of each wave -------------------------------------
+      {
+        float ms[N], ls[N];
+        bcast_all<R>(m, ms);
+        bcast_all<R>(l, ls);
+  #pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+  #pragma unroll
+          for (int j = 0; j < N; ++j) {
+            const float mo = __shfl_xor(ms[j], off);
+            const float lo = __shfl_xor(ls[j], off);
+            const float mn = fmaxf(ms[j], mo);
+            const float ca = fast_exp2(ms[j] - mn);
+            const float cb = fast_exp2(mo - mn);
+            ls[j] = ls[j] * ca + lo * cb;
+            ms[j] = mn;
+  #pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              acc[j][e] = acc[j][e] * ca + __shfl_xor(acc[j][e], off) * cb;
+          }
+        }
+        // ---- merge the waves through LDS ------------------------------------------
+        if (row == 0) {
+  #pragma unroll
+          for (int j = 0; j < N; ++j)
+  #pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
+          if ((li & (W - 1)) == 0) {
+            sm_m[wave][own] = ms[0];
+            sm_l[wave][own] = ls[0];
+          }
+        }
+      }
+      __syncthreads();
+      {
+        const bool direct = cur.slot < 0;
+        for (int o = tid; o < N * D; o += kThreads) {
+          const int h = o / D;
+          const int d = o - h * D;
+          float M = sm_m[0][h];
+  #pragma unroll
+          for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+          float lsum = 0.f, osum = 0.f;
+  #pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float c = fast_exp2(sm_m[w][h] - M);
+            lsum += sm_l[w][h] * c;
+            osum += sm_acc[w][h][d] * c;
+          }
+          const float val = lsum > 0.f ? osum / lsum : 0.f;
+          const int qh = cur.g * N + h;
+          if (direct) {
+            store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
+          } else {
+            const int64_t pi = static_cast<int64_t>(cur.slot) * N + h;
+            store_shared(a.part_o + pi * D + d, val);
+            if (d == 0) {
+              store_shared(a.part_ml + pi * 2 + 0, M);
+              store_shared(a.part_ml + pi * 2 + 1, lsum);
+            }
+          }
+        }
+      }
+      __syncthreads();   // LDS merge buffers are reused by the next segment
+      if (cur.slot >= 0) {
+        if (cur.slot & 1) { pb_s = cur.s; pb_g = cur.g; }
+        else { pa_s = cur.s; pa_g = cur.g; }
+      }
+      if (!has_next) break;
+
+      // ---- move on: loads of the segment after next, then the next segment's
+      // primed ring blocks (in that order, so the primed blocks are the
+      // youngest loads)
+      cur = nxt;
+      pos = pos_n;
+      pos_n = next_pos(cur, pos);
+      has_next = pos_n < pos_end;
+      if (has_next) {
+        nxt = seg_at(pos_n);
+        has_next = nxt.blk1 > nxt.blk0;
+      }
+      tbl = tbl_nxt;
+      load_q(cur, qv);
+      tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
+      c0 = cur.blk0;
+      nk = chunk_blocks(cur, c0);
+      lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
+      m = kNegBig;
+      l = 0.f;
+  #pragma unroll
+      for (int j = 0; j < N; ++j)
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+      n0 = issue(0, k0, v0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kRing == 3) n1 = issue(1, k1, v1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    if (sm_last[0]) {
-      const int A = pair_start(pa_s, pa_g);
-      merge_pair<T, D, N, kThreads>(a, pa_s, pa_g, A - C, A, A + nb_of(pa_s), Q, tid);
-      if (tid == 0)
-        __hip_atomic_store(a.counters + pa_s * Hkv + pa_g, 0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+
     }
-    if (sm_last[1]) {
-      const int A = pair_start(pb_s, pb_g);
-      merge_pair<T, D, N, kThreads>(a, pb_s, pb_g, A - C, A, A + nb_of(pb_s), Q, tid);
-      if (tid == 0)
-        __hip_atomic_store(a.counters + pb_s * Hkv + pb_g, 0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (!split) break;
+
+    // ---- arrivals of this unit's pieces -------------------------------------------
+    // Publication: every wave waits until its piece stores (device-coherent
+    // atomic stores) are complete, then the workgroup barrier, then thread 0
+    // counts the pieces with an agent-scope add; the add therefore reaches
+    // memory after every piece store of the workgroup.  Acquisition: the
+    // workgroup whose add completes a pair runs an agent-scope acquire fence
+    // before the barrier that releases its threads to the merge, whose loads
+    // are device-coherent atomic loads.  The add itself is relaxed: an
+    // agent-scope release would add an L2 write-back (buffer_wbl2) per
+    // workgroup, which publishes plain stores this protocol does not use and
+    // cost 15 us a call on the 64-sequence random-length batch.  The last
+    // arrival of a pair merges its pieces and leaves the counter at zero for
+    // the next call.
+    if (pa_s >= 0 || pb_s >= 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // work position of the pair's block 0; its work range starts C earlier
+      auto pair_start = [&](int q, int g) { return Hkv * sm_pre[q] + g * cost_of(q) + C; };
+      auto pieces = [&](int q, int g) {
+        const int A = pair_start(q, g);
+        return up.of(A + nb_of(q) - 1) - up.of(A) + 1;
+      };
+      if (tid == 0) {
+        int last_a = 0, last_b = 0;
+        if (pa_s >= 0)
+          last_a = __hip_atomic_fetch_add(a.counters + pa_s * Hkv + pa_g, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == pieces(pa_s, pa_g) - 1;
+        if (pb_s >= 0)
+          last_b = __hip_atomic_fetch_add(a.counters + pb_s * Hkv + pb_g, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == pieces(pb_s, pb_g) - 1;
+        if (last_a | last_b) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sm_last[0] = last_a;
+        sm_last[1] = last_b;
+      }
+      __syncthreads();
+      if (sm_last[0]) {
+        const int A = pair_start(pa_s, pa_g);
+        merge_pair<T, D, N, kThreads>(a, pa_s, pa_g, A - C, A, A + nb_of(pa_s), up, tid);
+        if (tid == 0)
+          __hip_atomic_store(a.counters + pa_s * Hkv + pa_g, 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (sm_last[1]) {
+        const int A = pair_start(pb_s, pb_g);
+        merge_pair<T, D, N, kThreads>(a, pb_s, pb_g, A - C, A, A + nb_of(pb_s), up, tid);
+        if (tid == 0)
+          __hip_atomic_store(a.counters + pb_s * Hkv + pb_g, 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+
+    // ---- the next unit: a chunk, while there are any ----------------------------
+    if (up.U == up.G) break;
+    if (tid == 0)
+      sm_unit = up.G + __hip_atomic_fetch_add(ctl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    u = sm_unit;
+    __syncthreads();
+    if (u >= up.U) break;
+  }
+  // the last workgroup to finish leaves both counters at zero for the next call
+  // (every other workgroup has taken its last unit by then)
+  if (split && up.U > up.G && tid == 0) {
+    if (__hip_atomic_fetch_add(ctl + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        static_cast<int>(gridDim.x) - 1) {
+      __hip_atomic_store(ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -424,9 +424,9 @@ pa_status prepare_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const 
     return fail(PA_ERR_UNSUPPORTED, "num_seqs %d (at most %d)", seqs->num_seqs,
                 pa::kMaxDecodeSeqs);
   if (plan->workspace_bytes > 0 &&
-      static_cast<int64_t>(seqs->num_seqs) * pool->num_kv_heads > pa::kCounterSlots)
+      static_cast<int64_t>(seqs->num_seqs) * pool->num_kv_heads > pa::kPairSlots)
     return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads = %lld (at most %d when split)",
-                static_cast<long long>(seqs->num_seqs) * pool->num_kv_heads, pa::kCounterSlots);
+                static_cast<long long>(seqs->num_seqs) * pool->num_kv_heads, pa::kPairSlots);
   *a = pa::DecodeArgs{};
   a->q = q;
   a->out = out;
@@ -585,22 +585,29 @@ pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
   if (hs != PA_OK) return hs;
   info->workgroups = grid;
   // the kernel's plan, from the host copy of the lengths: pair (s, g) owns
-  // nb_s blocks priced nb_s + seg_cost, laid end to end; split, slice i
-  // covers work [i Q, (i + 1) Q)
+  // nb_s blocks priced nb_s + seg_cost, laid end to end; split, the work is cut
+  // into the static slices and handed-out chunks of pa::unit_plan
   const int H = pool->num_kv_heads;
   const int C = a.seg_cost;
   int64_t B = 0;
+  int nb_lo = 0x7fffffff, nb_hi = 0;
   for (int s = 0; s < seqs->num_seqs; ++s) {
     int L = host_context_lens[s];
     L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
-    if (L > 0) B += static_cast<int64_t>(H) * ((L + pa::kUnit - 1) / pa::kUnit + C);
+    if (L == 0) continue;
+    const int nb = (L + pa::kUnit - 1) / pa::kUnit;
+    B += static_cast<int64_t>(H) * (nb + C);
+    nb_lo = nb < nb_lo ? nb : nb_lo;
+    nb_hi = nb > nb_hi ? nb : nb_hi;
   }
-  int64_t Q = 0;
+  pa::UnitPlan up{};
   if (a.min_slice_blocks > 0) {
-    Q = (B + grid - 1) / grid;
-    if (Q < a.min_slice_blocks) Q = a.min_slice_blocks;
+    up = pa::unit_plan(static_cast<int32_t>(B), grid, a.min_slice_blocks, a.max_slices,
+                       nb_lo >= nb_hi);
+    info->slice_blocks = up.Q1;
+    info->chunk_blocks = up.U > up.G ? up.Q2 : 0;
+    info->units = up.U;
   }
-  info->slice_blocks = static_cast<int32_t>(Q);
   int64_t pairs = 0, pieces = 0, pre = 0;
   int32_t most = 0;
   for (int s = 0; s < seqs->num_seqs; ++s) {
@@ -610,7 +617,9 @@ pa_status pa_decode_split_info(const pa_kv_pool* pool, const pa_seq_desc* seqs,
     const int64_t nb = (L + pa::kUnit - 1) / pa::kUnit;
     for (int g = 0; g < H; ++g) {
       const int64_t A = H * pre + g * (nb + C) + C;   // work position of the pair's block 0
-      const int64_t n = Q > 0 ? (A + nb - 1) / Q - A / Q + 1 : 1;
+      const int64_t n = a.min_slice_blocks > 0
+                            ? up.of(static_cast<int32_t>(A + nb - 1)) - up.of(static_cast<int32_t>(A)) + 1
+                            : 1;
       ++pairs;
       pieces += n;
       if (n > most) most = static_cast<int32_t>(n);

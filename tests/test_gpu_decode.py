@@ -91,6 +91,57 @@ def test_one_long_pair_in_many_pieces(num_q_heads, num_kv_heads):
     _full_check(w)
 
 
+@pytest.mark.parametrize("partition_size", [16, 64, 1024])
+def test_chunks_handed_out(partition_size):
+    """Mixed context lengths: the static slices cover nine tenths of the work
+    and the rest goes out in chunks that the workgroups take as they finish.
+    Three calls in a row on one workspace: each equals the oracle and the
+    first call bit for bit (whichever workgroup takes a chunk, it computes the
+    same piece), and the counters of the workspace header, the chunk hand-out
+    ones included, are zero afterwards."""
+    from paged_kv_cache_87_amd import binding as pa
+    rng = np.random.default_rng(740 + partition_size)
+    lens = [int(x) for x in rng.integers(1, 2049, size=64)]
+    nb = sum((x + 15) // 16 for x in lens) + 16
+    w = wl.decode_workload(f"chunks_p{partition_size}", 740 + partition_size, dtype=wl.BF16,
+                           num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                           num_blocks=nb, context_lens=lens, partition_size=partition_size)
+    g = runner.GpuStep(w)
+    split = pa.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, partition_size)
+    announce(f"{w.name} split {split}")
+    assert split["chunk_blocks"] > 0 and split["units"] > split["workgroups"], split
+    g.write_history()
+    g.append()
+    ws = pa.decode_workspace(g.pool, g.seqs, w.num_q_heads, partition_size)
+    _, _, _, out_ref = oracle_step(w)
+    first = None
+    for it in range(3):
+        g.out.zero_()
+        pa.pa_decode(g.pool, g.seqs, g.q, g.out, w.scale, partition_size, ws)
+        torch.cuda.synchronize()
+        assert_close(g.out_f64(), out_ref, w.dtype, f"{w.name} call {it}")
+        if first is None:
+            first = g.out.clone()
+        else:
+            assert torch.equal(g.out.view(torch.uint8), first.view(torch.uint8)), it
+    assert int(ws[:256 * 1024].count_nonzero()) == 0
+
+
+def test_equal_lengths_stay_static():
+    """Equal context lengths: the static slices cover all the work (no
+    chunks), as before the hand-out existed."""
+    from paged_kv_cache_87_amd import binding as pa
+    w = wl.decode_workload("equal_lengths", 745, dtype=wl.BF16, num_q_heads=32, num_kv_heads=8,
+                           head_dim=128, block_size=16, num_blocks=4200,
+                           context_lens=[1000] * 64, partition_size=64)
+    g = runner.GpuStep(w)
+    split = pa.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, 64)
+    announce(f"{w.name} split {split}")
+    assert split["chunk_blocks"] == 0 and split["units"] == split["workgroups"], split
+    del g
+    _full_check(w)
+
+
 @pytest.mark.parametrize("partition_size", [0, 16])
 def test_largest_batch(partition_size):
     """4096 sequences, the most one call takes (the work plan every workgroup
