@@ -192,55 +192,59 @@ constexpr int kSegCost = 24;
 // as kSegCost more) is cut into G static slices of Q1, one per workgroup, and
 // after them into chunks of Q2 that the workgroups take one at a time as they
 // finish (a counter in the workspace header hands them out): workgroups that
-// run slower take fewer.  The static slices cover kStaticNum / kStaticDen of
-// the work.  When every non-empty pair has the same length the slices alone
+// run slower take fewer.  The static slices cover nine tenths of the work.  When every non-empty pair has the same length the slices alone
 // cover it (equal work per workgroup, and the slices usually cut no pair), as
 // they do when the chunks would not fit the partial slots (kMaxSlices units).
 // Unit u's pieces go to partial slots 2u (its first segment) and 2u + 1 (its
 // last).  Shared by the kernel and the host's description of the split.
-constexpr int kStaticNum = 9;
-constexpr int kStaticDen = 10;
+constexpr int kStaticTenths = 9;     // the static slices cover B - floor(B / 10) * (10 - 9)
 constexpr int kChunkDiv = 16;        // chunk = static slice / kChunkDiv (at least min_slice)
-__host__ __device__ inline int64_t imax64(int64_t x, int64_t y) { return x > y ? x : y; }
-__host__ __device__ inline int64_t imin64(int64_t x, int64_t y) { return x < y ? x : y; }
 struct UnitPlan {
   int32_t G, Q1, Q2, Bs, B, U;
   __host__ __device__ int32_t start(int32_t u) const {
-    return u < G ? static_cast<int32_t>(imin64(static_cast<int64_t>(u) * Q1, Bs))
+    return u < G ? static_cast<int32_t>(static_cast<uint32_t>(u) * Q1 < static_cast<uint32_t>(Bs)
+                                            ? static_cast<uint32_t>(u) * Q1
+                                            : static_cast<uint32_t>(Bs))
                  : Bs + (u - G) * Q2;
   }
   __host__ __device__ int32_t end(int32_t u) const {
-    return u < G ? static_cast<int32_t>(imin64(static_cast<int64_t>(u + 1) * Q1, Bs))
-                 : static_cast<int32_t>(imin64(Bs + static_cast<int64_t>(u - G + 1) * Q2, B));
+    return u < G ? start(u + 1)
+                 : (static_cast<uint32_t>(u - G + 1) * Q2 < static_cast<uint32_t>(B - Bs)
+                        ? Bs + (u - G + 1) * Q2
+                        : B);
   }
   __host__ __device__ int32_t of(int32_t pos) const {
     return pos < Bs ? pos / Q1 : G + (pos - Bs) / Q2;
   }
 };
+// All in 32-bit unsigned arithmetic (B < 2^31, G <= 2048, so no sum below
+// overflows), the same on the host and the device.
 __host__ __device__ inline UnitPlan unit_plan(int32_t B, int32_t G, int32_t min_slice,
                                               int32_t max_units, bool equal_pairs) {
+  const uint32_t b = static_cast<uint32_t>(B), g = static_cast<uint32_t>(G);
+  const uint32_t ms = static_cast<uint32_t>(min_slice > 1 ? min_slice : 1);
   UnitPlan p;
   p.B = B;
   p.G = G;
-  const int64_t q = imax64(imax64((static_cast<int64_t>(B) + G - 1) / G, min_slice), 1);
-  const int64_t q1 = imax64(imax64((static_cast<int64_t>(kStaticNum) * B +
-                                    static_cast<int64_t>(kStaticDen) * G - 1) /
-                                       (static_cast<int64_t>(kStaticDen) * G),
-                                   min_slice),
-                            1);
-  const int64_t bs = imin64(B, q1 * G);
-  const int64_t q2 = imax64(imax64(q1 / kChunkDiv, min_slice), 1);
-  const int64_t chunks = (B - bs + q2 - 1) / q2;
-  if (equal_pairs || chunks == 0 || G + chunks > max_units) {
+  uint32_t q = (b + g - 1) / g;
+  q = q > ms ? q : ms;
+  const uint32_t stat = b - (b / 10) * (10 - kStaticTenths);   // work of the static slices
+  uint32_t q1 = (stat + g - 1) / g;
+  q1 = q1 > ms ? q1 : ms;
+  const uint32_t bs = static_cast<uint64_t>(q1) * g < b ? q1 * g : b;
+  uint32_t q2 = q1 / kChunkDiv;
+  q2 = q2 > ms ? q2 : ms;
+  const uint32_t chunks = (b - bs + q2 - 1) / q2;
+  if (equal_pairs || chunks == 0 || g + chunks > static_cast<uint32_t>(max_units)) {
     p.Q1 = static_cast<int32_t>(q);
-    p.Bs = static_cast<int32_t>(imin64(B, q * G));
+    p.Bs = static_cast<int32_t>(static_cast<uint64_t>(q) * g < b ? q * g : b);
     p.Q2 = p.Q1;
     p.U = G;
   } else {
     p.Q1 = static_cast<int32_t>(q1);
     p.Bs = static_cast<int32_t>(bs);
     p.Q2 = static_cast<int32_t>(q2);
-    p.U = static_cast<int32_t>(G + chunks);
+    p.U = static_cast<int32_t>(g + chunks);
   }
   return p;
 }
