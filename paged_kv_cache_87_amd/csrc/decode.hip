@@ -525,320 +525,324 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       any = cur.blk1 > cur.blk0;     // else the unit holds no block
     }
     if (any) {
-    int c0 = cur.blk0;                 // first block of the current chunk
-    int nk = 0;                        // this wave's blocks in the current chunk
-    int2 tbl = load_tbl(cur, c0);
-    uint32_t qv[N][NW];
-    load_q(cur, qv);
-    uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
-    auto chunk_blocks = [&](const Seg& x, int cs) {
-      const int ce = min(x.blk1, cs + kChunkBlocks);
-      return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
-    };
-
-    float m = kNegBig, l = 0.f;
-    float acc[N][EPL];
-  #pragma unroll
-    for (int j = 0; j < N; ++j)
-  #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-
-    // Issue the loads of this wave's k-th unit of the current chunk into
-    // (kf, vf) and return the mask of its valid tokens (bit t: token 16 j + t).
-    // Past the wave's last unit, or for a table entry outside the pool, the
-    // descriptors have size 0: the loads return zeros without touching memory
-    // and the tokens of that block count as invalid.  Token rows 0 .. 7 of the
-    // unit (uu = 0, 1) come through the first descriptor, rows 8 .. 15 through
-    // the second, which is the first one again unless blocks hold 8 tokens.
-    auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
-      int phys = -1, phys2 = -1;
-      int nvalid = 0;
-      int sub = 0;                     // first token row of the unit inside its block
-      if (k < nk) {
-        const int j = c0 + wave + kWaves * k;
-        phys = __builtin_amdgcn_readlane(tbl.x, k);
-        phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
-        const int n = cur.tok1 - j * kUnit;
-        nvalid = n < kUnit ? n : kUnit;
-        sub = small ? 0 : (j << 4) & ((1 << bshift) - 1);
-      }
-      const bool ok = phys >= 0 && phys < a.num_blocks;
-      const bool ok2 = phys2 >= 0 && phys2 < a.num_blocks;
-      const int vmask = ((ok ? 0x00ff : 0) | (ok2 ? 0xff00 : 0)) & ((1 << nvalid) - 1);
-      const uint32_t sub_bytes = static_cast<uint32_t>(sub) * row_bytes;
-      const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride + sub_bytes : 0;
-      const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
-      const Rsrc rk = make_rsrc(kpool + off, size);
-      const Rsrc rv = make_rsrc(vpool + off, size);
-      const int64_t off2 = ok2 ? static_cast<int64_t>(phys2) * block_stride : 0;
-      const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
-      const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
-      const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
-  #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
-  #pragma unroll
-      for (int uu = 2; uu < 4; ++uu) kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
-  #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
-  #pragma unroll
-      for (int uu = 2; uu < 4; ++uu) vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
-      return vmask;
-    };
-
-    // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
-    // running max and sum, then P.V.  The reference max of a stream only moves
-    // when a score passes it by more than kRescaleLog2 (then the accumulators
-    // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
-    // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
-    auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
-      float z[4];
-  #pragma unroll
-      for (int uu = 0; uu < 4; ++uu) {
-        float part_dot[N];
-  #pragma unroll
-        for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
-        z[uu] = reduce_scatter<R>(part_dot) * sl2;
-      }
-      // tokens past the context (partial last unit, or a unit the ring runs
-      // past its end) or in a block outside the pool get no weight and a zero
-      // value row, whatever the pool holds there
-      if (vmask != 0xffff) {
-  #pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-          if (((vmask >> (row + 4 * uu)) & 1) == 0) {
-            z[uu] = -INFINITY;
-  #pragma unroll
-            for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
-          }
-        }
-      }
-      const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
-        const float m_new = mx > m + kRescaleLog2 ? mx : m;
-        const float alpha = fast_exp2(m - m_new);
-        m = m_new;
-        l *= alpha;
-        float alpha_j[N];
-        bcast_all<R>(alpha, alpha_j);
-  #pragma unroll
-        for (int j = 0; j < N; ++j)
-  #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
-      }
-      float p[4];
-  #pragma unroll
-      for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
-
-      if constexpr (sizeof(T) == 2) {
-        // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
-        // with one v_dot2_f32_bf16 per (head, element): the value rows of the
-        // pair are interleaved with v_perm, the weights packed to bf16.  The
-        // running sum adds the same rounded weights (slot 0 is the lane's own
-        // head), so the normalised output is a convex combination of the V rows.
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-  #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int ua = 2 * pr, ub = 2 * pr + 1;
-          float pa[N], pb[N];
-          bcast_all<R>(p[ua], pa);
-          bcast_all<R>(p[ub], pb);
-          uint32_t pw[N];
-  #pragma unroll
-          for (int j = 0; j < N; ++j) {
-            const f32x2 two = {pa[j], pb[j]};
-            pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
-          }
-          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[0]),
-                                              __builtin_bit_cast(bf16x2, 0x3f803f80u), l, false);
-  #pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            // element 2w: low halves of token a and b; element 2w+1: high halves
-            const uint32_t ve = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x05040100u);
-            const uint32_t vo = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x07060302u);
-  #pragma unroll
-            for (int j = 0; j < N; ++j) {
-              acc[j][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, ve), acc[j][2 * w],
-                  false);
-              acc[j][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, vo),
-                  acc[j][2 * w + 1], false);
-            }
-          }
-        }
-      } else {
-        l += (p[0] + p[1]) + (p[2] + p[3]);
-  #pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-          float pj[N];
-          bcast_all<R>(p[uu], pj);
-  #pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            const float v = frag_elem<T, D>(vf[uu], e);
-  #pragma unroll
-            for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
-          }
-        }
-      }
-    };
-
-    // ---- prologue: the first segment's table and query rows, then the next one's
-    // (left in flight), then the first segment's primed ring blocks --------------
-    __builtin_amdgcn_s_waitcnt(0);
-    int pos_n = next_pos(cur, pos);
-    bool has_next = pos_n < pos_end;
-    Seg nxt = has_next ? seg_at(pos_n) : cur;
-    has_next = has_next && nxt.blk1 > nxt.blk0;
-    int2 tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
-    nk = chunk_blocks(cur, c0);
-
-    F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
-    int n0 = issue(0, k0, v0);
-    __builtin_amdgcn_sched_barrier(0);
-    int n1 = 0;
-    if constexpr (kRing == 3) n1 = issue(1, k1, v1);
-    __builtin_amdgcn_sched_barrier(0);
-    int n2 = 0;
-
-    for (;;) {
-      // ---- the ring over this chunk of the current segment (one exit, at the
-      // bottom: a trip always runs every stage; stages past the wave's last
-      // block see size-0 descriptors and zero valid tokens and change nothing)
-      if constexpr (kRing == 2) {
-        for (int k = 0; k < nk; k += 2) {
-          n1 = issue(k + 1, k1, v1);
-          __builtin_amdgcn_sched_barrier(0);
-          process(k0, v0, n0);
-          n0 = issue(k + 2, k0, v0);
-          __builtin_amdgcn_sched_barrier(0);
-          process(k1, v1, n1);
-        }
-      } else {
-        for (int k = 0; k < nk; k += 3) {
-          n2 = issue(k + 2, k2, v2);
-          __builtin_amdgcn_sched_barrier(0);
-          process(k0, v0, n0);
-          n0 = issue(k + 3, k0, v0);
-          __builtin_amdgcn_sched_barrier(0);
-          process(k1, v1, n1);
-          n1 = issue(k + 4, k1, v1);
-          __builtin_amdgcn_sched_barrier(0);
-          process(k2, v2, n2);
-        }
-      }
-
-      // ---- a segment longer than one chunk: next chunk of the same segment -----
-      if (c0 + kChunkBlocks < cur.blk1) {
-        c0 += kChunkBlocks;
-        tbl = load_tbl(cur, c0);
-        __builtin_amdgcn_s_waitcnt(0);
-        nk = chunk_blocks(cur, c0);
-        n0 = issue(0, k0, v0);
-        __builtin_amdgcn_sched_barrier(0);
-        n1 = issue(1, k1, v1);
-        __builtin_amdgcn_sched_barrier(0);
-        continue;
-      }
-
-      // ---- merge the four rows of each wave -------------------------------------
-      {
-        float ms[N], ls[N];
-        bcast_all<R>(m, ms);
-        bcast_all<R>(l, ls);
-  #pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-  #pragma unroll
-          for (int j = 0; j < N; ++j) {
-            const float mo = __shfl_xor(ms[j], off);
-            const float lo = __shfl_xor(ls[j], off);
-            const float mn = fmaxf(ms[j], mo);
-            const float ca = fast_exp2(ms[j] - mn);
-            const float cb = fast_exp2(mo - mn);
-            ls[j] = ls[j] * ca + lo * cb;
-            ms[j] = mn;
-  #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              acc[j][e] = acc[j][e] * ca + __shfl_xor(acc[j][e], off) * cb;
-          }
-        }
-        // ---- merge the waves through LDS ------------------------------------------
-        if (row == 0) {
-  #pragma unroll
-          for (int j = 0; j < N; ++j)
-  #pragma unroll
-            for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
-          if ((li & (W - 1)) == 0) {
-            sm_m[wave][own] = ms[0];
-            sm_l[wave][own] = ls[0];
-          }
-        }
-      }
-      __syncthreads();
-      {
-        const bool direct = cur.slot < 0;
-        for (int o = tid; o < N * D; o += kThreads) {
-          const int h = o / D;
-          const int d = o - h * D;
-          float M = sm_m[0][h];
-  #pragma unroll
-          for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-          float lsum = 0.f, osum = 0.f;
-  #pragma unroll
-          for (int w = 0; w < kWaves; ++w) {
-            const float c = fast_exp2(sm_m[w][h] - M);
-            lsum += sm_l[w][h] * c;
-            osum += sm_acc[w][h][d] * c;
-          }
-          const float val = lsum > 0.f ? osum / lsum : 0.f;
-          const int qh = cur.g * N + h;
-          if (direct) {
-            store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
-          } else {
-            const int64_t pi = static_cast<int64_t>(cur.slot) * N + h;
-            store_shared(a.part_o + pi * D + d, val);
-            if (d == 0) {
-              store_shared(a.part_ml + pi * 2 + 0, M);
-              store_shared(a.part_ml + pi * 2 + 1, lsum);
-            }
-          }
-        }
-      }
-      __syncthreads();   // LDS merge buffers are reused by the next segment
-      if (cur.slot >= 0) {
-        if (cur.slot & 1) { pb_s = cur.s; pb_g = cur.g; }
-        else { pa_s = cur.s; pa_g = cur.g; }
-      }
-      if (!has_next) break;
-
-      // ---- move on: loads of the segment after next, then the next segment's
-      // primed ring blocks (in that order, so the primed blocks are the
-      // youngest loads)
-      cur = nxt;
-      pos = pos_n;
-      pos_n = next_pos(cur, pos);
-      has_next = pos_n < pos_end;
-      if (has_next) {
-        nxt = seg_at(pos_n);
-        has_next = nxt.blk1 > nxt.blk0;
-      }
-      tbl = tbl_nxt;
+      int c0 = cur.blk0;                 // first block of the current chunk
+      int nk = 0;                        // this wave's blocks in the current chunk
+      int2 tbl = load_tbl(cur, c0);
+      uint32_t qv[N][NW];
       load_q(cur, qv);
-      tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
-      c0 = cur.blk0;
-      nk = chunk_blocks(cur, c0);
-      lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
-      m = kNegBig;
-      l = 0.f;
-  #pragma unroll
+      uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
+      auto chunk_blocks = [&](const Seg& x, int cs) {
+        const int ce = min(x.blk1, cs + kChunkBlocks);
+        return ce - cs - wave > 0 ? (ce - cs - wave + kWaves - 1) / kWaves : 0;
+      };
+
+      float m = kNegBig, l = 0.f;
+      float acc[N][EPL];
+    #pragma unroll
       for (int j = 0; j < N; ++j)
-  #pragma unroll
+    #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
-      n0 = issue(0, k0, v0);
+
+      // Issue the loads of this wave's k-th unit of the current chunk into
+      // (kf, vf) and return the mask of its valid tokens (bit t: token 16 j + t).
+      // Past the wave's last unit, or for a table entry outside the pool, the
+      // descriptors have size 0: the loads return zeros without touching memory
+      // and the tokens of that block count as invalid.  Token rows 0 .. 7 of the
+      // unit (uu = 0, 1) come through the first descriptor, rows 8 .. 15 through
+      // the second, which is the first one again unless blocks hold 8 tokens.
+      auto issue = [&](int k, F (&kf)[4], F (&vf)[4]) {
+        int phys = -1, phys2 = -1;
+        int nvalid = 0;
+        int sub = 0;                     // first token row of the unit inside its block
+        if (k < nk) {
+          const int j = c0 + wave + kWaves * k;
+          phys = __builtin_amdgcn_readlane(tbl.x, k);
+          phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
+          const int n = cur.tok1 - j * kUnit;
+          nvalid = n < kUnit ? n : kUnit;
+          sub = small ? 0 : (j << 4) & ((1 << bshift) - 1);
+        }
+        const bool ok = phys >= 0 && phys < a.num_blocks;
+        const bool ok2 = phys2 >= 0 && phys2 < a.num_blocks;
+        const int vmask = ((ok ? 0x00ff : 0) | (ok2 ? 0xff00 : 0)) & ((1 << nvalid) - 1);
+        const uint32_t sub_bytes = static_cast<uint32_t>(sub) * row_bytes;
+        const int64_t off = ok ? static_cast<int64_t>(phys) * block_stride + sub_bytes : 0;
+        const uint32_t size = ok ? block_bytes - sub_bytes : 0u;
+        const Rsrc rk = make_rsrc(kpool + off, size);
+        const Rsrc rv = make_rsrc(vpool + off, size);
+        const int64_t off2 = ok2 ? static_cast<int64_t>(phys2) * block_stride : 0;
+        const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
+        const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
+        const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
+    #pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
+    #pragma unroll
+        for (int uu = 2; uu < 4; ++uu)
+          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
+    #pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
+    #pragma unroll
+        for (int uu = 2; uu < 4; ++uu)
+          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
+        return vmask;
+      };
+
+      // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
+      // running max and sum, then P.V.  The reference max of a stream only moves
+      // when a score passes it by more than kRescaleLog2 (then the accumulators
+      // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
+      // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
+      auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
+        float z[4];
+    #pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          float part_dot[N];
+    #pragma unroll
+          for (int idx = 0; idx < N; ++idx) part_dot[idx] = frag_dot<T, D>(qv[idx], kf[uu], 0.f);
+          z[uu] = reduce_scatter<R>(part_dot) * sl2;
+        }
+        // tokens past the context (partial last unit, or a unit the ring runs
+        // past its end) or in a block outside the pool get no weight and a zero
+        // value row, whatever the pool holds there
+        if (vmask != 0xffff) {
+    #pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            if (((vmask >> (row + 4 * uu)) & 1) == 0) {
+              z[uu] = -INFINITY;
+    #pragma unroll
+              for (int w = 0; w < NW; ++w) vf[uu].w[w] = 0u;
+            }
+          }
+        }
+        const float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
+          const float m_new = mx > m + kRescaleLog2 ? mx : m;
+          const float alpha = fast_exp2(m - m_new);
+          m = m_new;
+          l *= alpha;
+          float alpha_j[N];
+          bcast_all<R>(alpha, alpha_j);
+    #pragma unroll
+          for (int j = 0; j < N; ++j)
+    #pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha_j[j];
+        }
+        float p[4];
+    #pragma unroll
+        for (int uu = 0; uu < 4; ++uu) p[uu] = fast_exp2(z[uu] - m);
+
+        if constexpr (sizeof(T) == 2) {
+          // bf16: acc += p_a v_a + p_b v_b for token pairs (a, b) = (0, 1), (2, 3)
+          // with one v_dot2_f32_bf16 per (head, element): the value rows of the
+          // pair are interleaved with v_perm, the weights packed to bf16.  The
+          // running sum adds the same rounded weights (slot 0 is the lane's own
+          // head), so the normalised output is a convex combination of the V rows.
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+    #pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int ua = 2 * pr, ub = 2 * pr + 1;
+            float pa[N], pb[N];
+            bcast_all<R>(p[ua], pa);
+            bcast_all<R>(p[ub], pb);
+            uint32_t pw[N];
+    #pragma unroll
+            for (int j = 0; j < N; ++j) {
+              const f32x2 two = {pa[j], pb[j]};
+              pw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+            }
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[0]),
+                                                __builtin_bit_cast(bf16x2, 0x3f803f80u), l, false);
+    #pragma unroll
+            for (int w = 0; w < NW; ++w) {
+              // element 2w: low halves of token a and b; element 2w+1: high halves
+              const uint32_t ve = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x05040100u);
+              const uint32_t vo = __builtin_amdgcn_perm(vf[ub].w[w], vf[ua].w[w], 0x07060302u);
+    #pragma unroll
+              for (int j = 0; j < N; ++j) {
+                acc[j][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(
+                    __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, ve), acc[j][2 * w],
+                    false);
+                acc[j][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                    __builtin_bit_cast(bf16x2, pw[j]), __builtin_bit_cast(bf16x2, vo),
+                    acc[j][2 * w + 1], false);
+              }
+            }
+          }
+        } else {
+          l += (p[0] + p[1]) + (p[2] + p[3]);
+    #pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            float pj[N];
+            bcast_all<R>(p[uu], pj);
+    #pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+              const float v = frag_elem<T, D>(vf[uu], e);
+    #pragma unroll
+              for (int j = 0; j < N; ++j) acc[j][e] = fmaf(pj[j], v, acc[j][e]);
+            }
+          }
+        }
+      };
+
+      // ---- prologue: the first segment's table and query rows, then the next one's
+      // (left in flight), then the first segment's primed ring blocks --------------
+      __builtin_amdgcn_s_waitcnt(0);
+      int pos_n = next_pos(cur, pos);
+      bool has_next = pos_n < pos_end;
+      Seg nxt = has_next ? seg_at(pos_n) : cur;
+      has_next = has_next && nxt.blk1 > nxt.blk0;
+      int2 tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
+      nk = chunk_blocks(cur, c0);
+
+      F k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
+      int n0 = issue(0, k0, v0);
       __builtin_amdgcn_sched_barrier(0);
+      int n1 = 0;
       if constexpr (kRing == 3) n1 = issue(1, k1, v1);
       __builtin_amdgcn_sched_barrier(0);
-    }
+      int n2 = 0;
+
+      for (;;) {
+        // ---- the ring over this chunk of the current segment (one exit, at the
+        // bottom: a trip always runs every stage; stages past the wave's last
+        // block see size-0 descriptors and zero valid tokens and change nothing)
+        if constexpr (kRing == 2) {
+          for (int k = 0; k < nk; k += 2) {
+            n1 = issue(k + 1, k1, v1);
+            __builtin_amdgcn_sched_barrier(0);
+            process(k0, v0, n0);
+            n0 = issue(k + 2, k0, v0);
+            __builtin_amdgcn_sched_barrier(0);
+            process(k1, v1, n1);
+          }
+        } else {
+          for (int k = 0; k < nk; k += 3) {
+            n2 = issue(k + 2, k2, v2);
+            __builtin_amdgcn_sched_barrier(0);
+            process(k0, v0, n0);
+            n0 = issue(k + 3, k0, v0);
+            __builtin_amdgcn_sched_barrier(0);
+            process(k1, v1, n1);
+            n1 = issue(k + 4, k1, v1);
+            __builtin_amdgcn_sched_barrier(0);
+            process(k2, v2, n2);
+          }
+        }
+
+        // ---- a segment longer than one chunk: next chunk of the same segment -----
+        if (c0 + kChunkBlocks < cur.blk1) {
+          c0 += kChunkBlocks;
+          tbl = load_tbl(cur, c0);
+          __builtin_amdgcn_s_waitcnt(0);
+          nk = chunk_blocks(cur, c0);
+          n0 = issue(0, k0, v0);
+          __builtin_amdgcn_sched_barrier(0);
+          n1 = issue(1, k1, v1);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
+
+        // ---- merge the four rows of each wave -------------------------------------
+        {
+          float ms[N], ls[N];
+          bcast_all<R>(m, ms);
+          bcast_all<R>(l, ls);
+    #pragma unroll
+          for (int off = 16; off <= 32; off <<= 1) {
+    #pragma unroll
+            for (int j = 0; j < N; ++j) {
+              const float mo = __shfl_xor(ms[j], off);
+              const float lo = __shfl_xor(ls[j], off);
+              const float mn = fmaxf(ms[j], mo);
+              const float ca = fast_exp2(ms[j] - mn);
+              const float cb = fast_exp2(mo - mn);
+              ls[j] = ls[j] * ca + lo * cb;
+              ms[j] = mn;
+    #pragma unroll
+              for (int e = 0; e < EPL; ++e)
+                acc[j][e] = acc[j][e] * ca + __shfl_xor(acc[j][e], off) * cb;
+            }
+          }
+          // ---- merge the waves through LDS ------------------------------------------
+          if (row == 0) {
+    #pragma unroll
+            for (int j = 0; j < N; ++j)
+    #pragma unroll
+              for (int e = 0; e < EPL; ++e) sm_acc[wave][slot_head[j]][li * EPL + e] = acc[j][e];
+            if ((li & (W - 1)) == 0) {
+              sm_m[wave][own] = ms[0];
+              sm_l[wave][own] = ls[0];
+            }
+          }
+        }
+        __syncthreads();
+        {
+          const bool direct = cur.slot < 0;
+          for (int o = tid; o < N * D; o += kThreads) {
+            const int h = o / D;
+            const int d = o - h * D;
+            float M = sm_m[0][h];
+    #pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+            float lsum = 0.f, osum = 0.f;
+    #pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+              const float c = fast_exp2(sm_m[w][h] - M);
+              lsum += sm_l[w][h] * c;
+              osum += sm_acc[w][h][d] * c;
+            }
+            const float val = lsum > 0.f ? osum / lsum : 0.f;
+            const int qh = cur.g * N + h;
+            if (direct) {
+              store_out<T>(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + qh) * D + d, val);
+            } else {
+              const int64_t pi = static_cast<int64_t>(cur.slot) * N + h;
+              store_shared(a.part_o + pi * D + d, val);
+              if (d == 0) {
+                store_shared(a.part_ml + pi * 2 + 0, M);
+                store_shared(a.part_ml + pi * 2 + 1, lsum);
+              }
+            }
+          }
+        }
+        __syncthreads();   // LDS merge buffers are reused by the next segment
+        if (cur.slot >= 0) {
+          if (cur.slot & 1) { pb_s = cur.s; pb_g = cur.g; }
+          else { pa_s = cur.s; pa_g = cur.g; }
+        }
+        if (!has_next) break;
+
+        // ---- move on: loads of the segment after next, then the next segment's
+        // primed ring blocks (in that order, so the primed blocks are the
+        // youngest loads)
+        cur = nxt;
+        pos = pos_n;
+        pos_n = next_pos(cur, pos);
+        has_next = pos_n < pos_end;
+        if (has_next) {
+          nxt = seg_at(pos_n);
+          has_next = nxt.blk1 > nxt.blk0;
+        }
+        tbl = tbl_nxt;
+        load_q(cur, qv);
+        tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
+        c0 = cur.blk0;
+        nk = chunk_blocks(cur, c0);
+        lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
+        m = kNegBig;
+        l = 0.f;
+    #pragma unroll
+        for (int j = 0; j < N; ++j)
+    #pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+        n0 = issue(0, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kRing == 3) n1 = issue(1, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
     }
     if (!split) break;
