@@ -336,11 +336,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     for (int t = 0; t < kHalves; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
+      // K fragments two products ahead, the order pinned: each product waits
+      // only for a read issued two products earlier (~2 % over the
+      // compiler's own order, which waited on each pair of reads)
+      constexpr int kAhead = 2;
+      uint4 kq[kD / 16];
+#pragma unroll
+      for (int kk = 0; kk < kAhead; ++kk)
+        kq[kk] = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * t + col][16 * kk + 8 * half]);
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
-        const uint4 kx = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * t + col][16 * kk + 8 * half]);
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qf[kk],
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kq[kk]), qf[kk],
                                                          st[t], 0, 0, 0);
+        if (kk + kAhead < kD / 16)
+          kq[kk + kAhead] = *reinterpret_cast<const uint4*>(
+              &sm.k[buf][32 * t + col][16 * (kk + kAhead) + 8 * half]);
+      }
+      // schedule: kAhead LDS reads (mask 0x100), then one product (0x008) and
+      // one read at a time
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kk + kAhead < kD / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     // ---- per half: causal mask, online softmax, O^T += V^T . P^T ------------
