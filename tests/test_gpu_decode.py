@@ -413,3 +413,36 @@ def test_unrelated_hip_error_is_not_blamed_on_a_launch():
     k_ref, v_ref, _, out_ref = oracle_step(w)
     assert_pools_equal(g, k_ref, v_ref)
     assert_close(g.out_f64(), out_ref, w.dtype, w.name)
+
+
+def _random_case(i):
+    """A seeded random decode batch: shapes, lengths (with empty and
+    one-token contexts), block size, head grouping, dtype and partition."""
+    rng = np.random.default_rng(7700 + i)
+    S = int(rng.choice([1, 2, 3, 7, 16, 33, 100]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    n_rep = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([8, 16, 32, 64]))
+    dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        lens = rng.integers(1, 300, size=S)
+    elif kind == 1:
+        lens = rng.integers(1, 3000, size=S)
+    else:
+        lens = rng.choice([0, 1, 15, 16, 17, 255, 1000, 2047], size=S)
+    lens = [int(x) for x in lens]
+    part = int(rng.choice([0, 16, 32, 64, 256, 1024]))
+    nb = sum((x + B - 1) // B for x in lens) + 8
+    return wl.decode_workload(f"random_{i}", 7700 + i, dtype=dtype, num_q_heads=Hkv * n_rep,
+                              num_kv_heads=Hkv, head_dim=D, block_size=B, num_blocks=nb,
+                              context_lens=lens, partition_size=part)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_batches(i):
+    """Seeded random batches over shapes, lengths, block sizes, dtypes and
+    partition sizes (the split's slices and handed-out chunks at many
+    shapes), every pool byte and output row against the oracle."""
+    _full_check(_random_case(i))

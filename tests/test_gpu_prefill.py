@@ -352,3 +352,29 @@ def test_validate_mode_rejects_long_q_len(monkeypatch):
         pa.pa_prefill(g.pool, short, g.q, g.out, g.q_start_loc, 30, w.scale)
     pa.pa_prefill(g.pool, g.seqs, g.q, g.out, g.q_start_loc, 30, w.scale)   # valid: runs
     torch.cuda.synchronize()
+
+
+def _random_prefill_case(i):
+    """A seeded random prefill batch: whole prompts and continuations (new
+    tokens after a history), one-token rows, block sizes, head grouping,
+    head_dim and dtype."""
+    rng = np.random.default_rng(7800 + i)
+    S = int(rng.choice([1, 2, 5, 9]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    n_rep = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([8, 16, 32, 128]))
+    dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
+    lens = [int(x) for x in rng.integers(1, 700, size=S)]
+    q_lens = [int(min(L, rng.choice([1, 7, 33, 130, L]))) for L in lens]
+    nb = sum((x + B - 1) // B for x in lens) + 8
+    return wl.prefill_workload(f"prefill_random_{i}", 7800 + i, dtype=dtype,
+                               num_q_heads=Hkv * n_rep, num_kv_heads=Hkv, head_dim=D,
+                               block_size=B, num_blocks=nb, context_lens=lens, q_lens=q_lens)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_random_batches(i):
+    """Seeded random prefill batches (shapes, prompt and continuation lengths,
+    block sizes, dtypes): every pool byte and output row against the oracle."""
+    _full(_random_prefill_case(i))
