@@ -29,6 +29,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -65,11 +66,28 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+DECODE_SOURCES = ("decode.hip", "pa_device.h", "pa_internal.h")
+
+
+def code_text(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the
+    compiler sees, so an edit of a comment keeps the decode's hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the decode kernel's sources (the kernel, the device helpers
+    and the plan it shares with the host), comments and layout ignored."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "pa_device.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_87_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in DECODE_SOURCES:
+        if read is None:
+            with open(os.path.join(ROOT, "paged_kv_cache_87_amd", "csrc", name)) as f:
+                text = f.read()
+        else:
+            text = read(name)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,9 +8,10 @@
 // Work decomposition
 //   A persistent grid of workgroups (eight waves, one workgroup per CU; four
 //   for the register-heavy variants) walks segments of (sequence, KV head)
-//   pairs: whole pairs, or equal slices of the batch's work when the context
-//   is split (see the driver below); the waves of a workgroup take a
-//   segment's blocks round-robin.
+//   pairs: whole pairs, or, when the context is split, an equal static slice
+//   of the batch's work per workgroup and then chunks handed out as the
+//   workgroups finish (see the driver below); the waves of a workgroup take
+//   a segment's blocks round-robin.
 //   Inside a wave the 64 lanes form four 16-lane DPP rows.  Row r handles
 //   tokens r, r+4, r+8, r+12 of the wave's current 16-token block; lane i of
 //   the row owns elements [i*D/16, (i+1)*D/16) of the head dimension, so one
