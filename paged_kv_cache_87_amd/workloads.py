@@ -206,7 +206,7 @@ def decode_workload(name, seed, *, dtype, num_q_heads, num_kv_heads, head_dim,
         raise ValueError("every context must extend past the shared prefix")
     nblk = [_ceil_div(int(L), block_size) for L in context_lens]
     if width is None:
-        width = max(nblk) if nblk else 1
+        width = max(max(nblk), 1) if nblk else 1
     tables = _tables(rng, nblk, num_blocks, width, shared_prefix_tokens // block_size)
     hist_start = np.zeros(S, dtype=np.int32)
     if shared_prefix_tokens:
@@ -244,7 +244,7 @@ def prefill_workload(name, seed, *, dtype, num_q_heads, num_kv_heads, head_dim,
     q_lens = context_lens.copy() if q_lens is None else np.asarray(q_lens, dtype=np.int32)
     nblk = [_ceil_div(int(L), block_size) for L in context_lens]
     if width is None:
-        width = max(nblk) if nblk else 1
+        width = max(max(nblk), 1) if nblk else 1
     tables = _tables(rng, nblk, num_blocks, width)
     hist_start = np.zeros(S, dtype=np.int32)
     # more new tokens than the context holds: nothing was written before
