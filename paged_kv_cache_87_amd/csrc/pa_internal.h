@@ -192,12 +192,14 @@ constexpr int kSegCost = 24;
 // as kSegCost more) is cut into G static slices of Q1, one per workgroup, and
 // after them into chunks of Q2 that the workgroups take one at a time as they
 // finish (a counter in the workspace header hands them out): workgroups that
-// run slower take fewer.  The static slices cover nine tenths of the work.  When every non-empty pair has the same length the slices alone
-// cover it (equal work per workgroup, and the slices usually cut no pair), as
-// they do when the chunks would not fit the partial slots (kMaxSlices units).
-// Unit u's pieces go to partial slots 2u (its first segment) and 2u + 1 (its
-// last).  Shared by the kernel and the host's description of the split.
-constexpr int kStaticTenths = 9;     // the static slices cover B - floor(B / 10) * (10 - 9)
+// run slower take fewer.  The static slices cover B - floor(B / 10), nine
+// tenths of the work.  When every non-empty pair has the same length the
+// slices alone cover it (equal work per workgroup, and the slices usually cut
+// no pair), as they do when the chunks would not fit the partial slots
+// (kMaxSlices units).  Unit u's pieces go to partial slots 2u (its first
+// segment) and 2u + 1 (its last).  Shared by the kernel and the host's
+// description of the split.
+constexpr int kStaticTenths = 9;     // tenths of the work the static slices cover
 constexpr int kChunkDiv = 16;        // chunk = static slice / kChunkDiv (at least min_slice)
 struct UnitPlan {
   int32_t G, Q1, Q2, Bs, B, U;
