@@ -17,7 +17,7 @@
 //   staged in LDS as [key][d] rows, double-buffered: at the start of a tile
 //   the next tile's K/V (loaded during the previous tile) are stashed and
 //   the loads of the tile after that are issued, so every load has a whole
-//   tile of math to arrive.  32-key tiles keep the kernel at 164 VGPRs and
+//   tile of math to arrive.  32-key tiles keep the kernel at 162 VGPRs and
 //   39 KB of LDS, so three workgroups (three waves per SIMD) share a CU; with
 //   64-key tiles it needed 198 VGPRs and 70 KB, two per CU, and ran ~6 %
 //   slower.
