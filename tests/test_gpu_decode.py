@@ -440,7 +440,7 @@ def _random_case(i):
                               context_lens=lens, partition_size=part)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_batches(i):
     """Seeded random batches over shapes, lengths, block sizes, dtypes and
     partition sizes (the split's slices and handed-out chunks at many

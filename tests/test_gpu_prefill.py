@@ -373,7 +373,7 @@ def _random_prefill_case(i):
                                block_size=B, num_blocks=nb, context_lens=lens, q_lens=q_lens)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(24))
 def test_prefill_random_batches(i):
     """Seeded random prefill batches (shapes, prompt and continuation lengths,
     block sizes, dtypes): every pool byte and output row against the oracle."""
