@@ -6,7 +6,8 @@ head_dim 128, bf16 K/V, block size 16, contexts uniform in [1, 8192]
 hot path for one new token per sequence: slot mapping and the K/V write of
 the new token (one fused launch), and the partitioned decode kernel (whose last partition of each
 sequence and KV head does the log-sum-exp merge), all through libpa.so on torch's current stream, with every input already
-resident in HBM.
+resident in HBM.  Before the warm-up steps, 50 ms of a read stream over a
+buffer of its own brings the GPU to its steady clocks (reported in the line).
 
 Printed: one JSON line with whole-step throughput (K/V bytes read per
 second), the decode call's roofline (K/V bytes / decode kernel time against
