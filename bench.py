@@ -220,14 +220,16 @@ class HipEvents:
 _EVENTS = None
 
 
-def timed(torch, stream, K, W, prefix, body, suffix=None):
+def timed(torch, stream, K, W, prefix, body, suffix=None, settle=False):
     """Run W untimed then K timed iterations; each iteration is prefix(),
-    body() bracketed by timing-only events, suffix().  Returns
-    (total ms / K, [body ms])."""
+    body() bracketed by timing-only events, suffix().  With settle, the GPU
+    first runs gpu_settle (steady clocks).  Returns (total ms / K, [body ms])."""
     global _EVENTS
     if _EVENTS is None:
         _EVENTS = HipEvents(torch)
     E = _EVENTS
+    if settle:
+        gpu_settle(torch, stream)
     for _ in range(W):
         prefix()
         body()
@@ -286,7 +288,7 @@ def secondary(torch, np, stream, K, W, partition_size):
         w = wl.llama_gqa_decode(pool_fill="zero", partition_size=partition_size)
         g = runner.GpuStep(w, layout=layout)
         g.write_history()
-        _, dec_ms = timed(torch, stream, K, W, g.append, g.attend)
+        _, dec_ms = timed(torch, stream, K, W, g.append, g.attend, settle=True)
         dec = float(np.mean(dec_ms))
         out["decode_layouts"][layout] = {
             "decode_us": dec * 1e3, "kv_GBps": w.kv_bytes_read() / (dec * 1e-3) / 1e9,
@@ -297,7 +299,8 @@ def secondary(torch, np, stream, K, W, partition_size):
     w = wl.batched_prefill(pool_fill="zero")
     g = runner.GpuStep(w)
     g.write_history()
-    step_ms, pre_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend)
+    step_ms, pre_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend,
+                            settle=True)
     lens = w.context_lens.astype(np.int64)
     flops = 2.0 * w.num_q_heads * w.head_dim * float(np.sum(lens * (lens + 1)))
     pre = float(np.mean(pre_ms))
@@ -317,7 +320,7 @@ def secondary(torch, np, stream, K, W, partition_size):
     g.write_history()
     from paged_kv_cache_87_amd import binding as _b
     lc_split = _b.pa_decode_split_info(g.pool, g.seqs, w.num_q_heads, w.partition_size)
-    step_ms, dec_ms = timed(torch, stream, K, W, g.append, g.attend)
+    step_ms, dec_ms = timed(torch, stream, K, W, g.append, g.attend, settle=True)
     dec = float(np.mean(dec_ms))
     logical = w.kv_bytes_read()
     prefix = w.meta["shared_prefix_tokens"]
@@ -343,7 +346,7 @@ def secondary(torch, np, stream, K, W, partition_size):
     src = perm[:pairs].to(torch.int32).cuda()
     dst = perm[pairs:2 * pairs].to(torch.int32).cuda()
     _, cp_ms = timed(torch, stream, K, W, lambda: None,
-                     lambda: binding.pa_copy_blocks(pool, src, dst))
+                     lambda: binding.pa_copy_blocks(pool, src, dst), settle=True)
     cp = float(np.mean(cp_ms))
     moved = 2 * 2 * pairs * 16 * 8 * 128 * 2          # read + write, K and V
     out["cow_copy_blocks"] = {
@@ -383,7 +386,7 @@ def secondary(torch, np, stream, K, W, partition_size):
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    _, cp_ms = timed(torch, stream, K, W, lambda: None, lambda: b.copy_(a))
+    _, cp_ms = timed(torch, stream, K, W, lambda: None, lambda: b.copy_(a), settle=True)
     out["hbm_copy_ceiling"] = {"bytes_moved": 2 << 30,
                                "GBps": (2 << 30) / (float(np.mean(cp_ms)) * 1e-3) / 1e9}
     out["hbm_copy_ceiling"]["frac_hbm_peak"] = out["hbm_copy_ceiling"]["GBps"] / HBM_PEAK_GBPS
@@ -393,7 +396,7 @@ def secondary(torch, np, stream, K, W, partition_size):
     # workgroup), the practical ceiling of a read-once kernel such as the decode
     words = torch.zeros(8192, dtype=torch.int32, device="cuda")
     _, rd_ms = timed(torch, stream, K, W, lambda: None,
-                     lambda: binding.pa_read_checksum(a, words, stream))
+                     lambda: binding.pa_read_checksum(a, words, stream), settle=True)
     out["hbm_read_ceiling"] = {"bytes_read": 1 << 30, "kernel": "pa_read_checksum, 8192 workgroups",
                                "GBps": (1 << 30) / (float(np.mean(rd_ms)) * 1e-3) / 1e9}
     out["hbm_read_ceiling"]["frac_hbm_peak"] = out["hbm_read_ceiling"]["GBps"] / HBM_PEAK_GBPS
