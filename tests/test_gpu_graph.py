@@ -1,11 +1,13 @@
-"""A decode step captured into a HIP graph: the fused slot mapping and K/V
+"""Steps captured into a HIP graph.  Decode: the fused slot mapping and K/V
 write (pa_append_kv) followed by the split decode, with the caller's
 workspace (pa_decode) or with the library's own array (pa_decode_noalloc).
-Neither records a memset or an allocation, and the decode leaves its
-counters at zero after every call, so a replayed step must equal the eager
-step bit for bit.  Between replays the program does eager work of its own
-(the output is poisoned) and synchronises; every replay is checked, and so is
-the oracle on the eager result."""
+Prefill: slot mapping, K/V write and the causal prefill of a mixed batch
+(decode rows, continuations and whole prompts), bf16 and fp32.  None of them
+records a memset or an allocation, and the decode leaves its counters at zero
+after every call, so a replayed step must equal the eager step bit for bit.
+Between replays the program does eager work of its own (the output is
+poisoned) and synchronises; every replay is checked, and so is the oracle on
+the eager result."""
 
 from __future__ import annotations
 
@@ -71,3 +73,39 @@ def test_decode_step_replays_in_a_graph(noalloc, partition_size):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(g.out.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_step_replays_in_a_graph(dtype):
+    lens = [700, 1, 2049, 40, 333, 4100]
+    q_lens = [700, 1, 300, 1, 17, 1]
+    w = wl.prefill_workload(f"graph_prefill_{dtype}", 4343, dtype=wl.BF16 if dtype == "bf16" else wl.F32,
+                            num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                            num_blocks=1024, context_lens=lens, q_lens=q_lens)
+    announce(f"{w.name} graph capture")
+    g = runner.GpuStep(w)
+    g.write_history()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.step()          # slot mapping, K/V write, prefill
+    torch.cuda.synchronize()
+    want = g.out.clone()
+    k_ref, v_ref, slots_ref, ref = oracle_step(w)
+    assert np.array_equal(g.slots.cpu().numpy(), slots_ref)
+    assert_close(want.double().cpu().numpy(), ref, w.dtype, w.name + " eager")
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        g.step()
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    for i in range(4):
+        g.out.fill_(float("nan"))
+        g.slots.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g.slots.cpu().numpy(), slots_ref), f"replay {i} slots"
+        assert torch.equal(g.out.view(bits), want.view(bits)), f"replay {i}"
