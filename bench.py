@@ -19,7 +19,8 @@ second), the decode call's roofline (K/V bytes / decode kernel time against
 whole step of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16), of the
 long-context shared-prefix decode, of the copy-on-write block copy and of
-the block swap between the device pool and a pinned host pool.
+the block swap between the device pool and a pinned host pool, and the
+decode step in one launch (pa_decode_step) against the two-launch step.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
@@ -322,6 +323,24 @@ def secondary(torch, np, stream, K, W, partition_size):
         out["decode_layouts"][layout] = {
             "decode_us": dec * 1e3, "kv_GBps": w.kv_bytes_read() / (dec * 1e-3) / 1e9,
             "frac_hbm_peak": w.kv_bytes_read() / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del g
+        torch.cuda.empty_cache()
+    # the decode step in one launch (pa_decode_step) against the two-launch
+    # step (pa_append_kv, then pa_decode), on the headline batch and on one
+    # sequence of 4096 tokens (partition 256), where launches weigh most
+    out["decode_step_fused"] = {}
+    for name, w in (("batch64", wl.llama_gqa_decode(pool_fill="zero",
+                                                    partition_size=partition_size)),
+                    ("batch1_ctx4096", wl.decode_workload(
+                        "gqa_b1", 87006, dtype=wl.BF16, num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, num_blocks=400, context_lens=[4096],
+                        partition_size=256, pool_fill="zero"))):
+        g = runner.GpuStep(w)
+        g.write_history()
+        two_ms, _ = timed(torch, stream, K, W, g.append, g.attend, settle=True)
+        one_ms, _ = timed(torch, stream, K, W, lambda: None, g.decode_step, settle=True)
+        out["decode_step_fused"][name] = {"two_launches_us_per_step": two_ms * 1e3,
+                                          "one_launch_us_per_step": one_ms * 1e3}
         del g
         torch.cuda.empty_cache()
     # batched causal prefill: slot mapping + write of every prompt token + prefill

@@ -364,6 +364,29 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_step -- one decode step in one launch: pa_append_kv (this
+ * step's K/V written to each sequence's newest slot) followed by pa_decode
+ * (attention over the whole history, the new token included), with the same
+ * results bit for bit (nanoserve Day 19, "What I added today": the step's
+ * K/V written to the cache, then attention over it in place; JuliaPagedAttn
+ * "API Reference": write_kv_cache! then paged_attention_cpu!).
+ *
+ * k_new, v_new and slot_mapping are those of pa_append_kv; q, out,
+ * num_q_heads, scale, partition_size and the workspace those of pa_decode.
+ * Inside the launch each new row is written to its slot once, and the
+ * attention takes the new token's K and V from k_new and v_new instead of
+ * reading the slot back, so no pool location is both written and read in
+ * the call.  As with pa_append_kv followed by pa_decode, the written slot
+ * must not be part of another sequence's context in the same call (the
+ * copy-on-write rule of the block allocator guarantees it).  Errors are
+ * those of both calls; nothing is launched on an error.
+ */
+pa_status pa_decode_step(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* k_new,
+                         const void* v_new, int64_t* slot_mapping, const void* q, void* out,
+                         int32_t num_q_heads, float scale, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_decode_noalloc -- pa_decode without a caller workspace, for callers
  * that cannot allocate device memory around the call: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.

@@ -41,7 +41,7 @@ EXPORTED = (
     "pa_allocator_allocate", "pa_allocator_fork", "pa_allocator_release",
     "pa_allocator_prepare_write", "pa_copy_blocks", "pa_swap_blocks", "pa_append_kv",
     "pa_decode_split_info", "pa_decode_noalloc", "pa_decode_noalloc_max_bytes",
-    "pa_read_checksum",
+    "pa_read_checksum", "pa_decode_step",
 )
 
 
@@ -105,6 +105,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pa_write_kv": (i32, [pool_p, vp, vp, vp, i32, vp]),
         "pa_decode_workspace_bytes": (sz, [pool_p, seq_p, i32, i32]),
         "pa_decode": (i32, [pool_p, seq_p, vp, vp, i32, f32, i32, vp, sz, vp]),
+        "pa_decode_step": (i32, [pool_p, seq_p, vp, vp, vp, vp, vp, i32, f32, i32, vp, sz, vp]),
         "pa_prefill": (i32, [pool_p, seq_p, vp, vp, vp, i32, i32, i32, f32, vp]),
         "pa_status_string": (ctypes.c_char_p, [i32]),
         "pa_last_error": (ctypes.c_char_p, []),
@@ -450,6 +451,40 @@ def pa_decode(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor, s
     return out
 
 
+def pa_decode_step(pool: KVPool, seqs: SeqDesc, k_new: torch.Tensor, v_new: torch.Tensor,
+                   q: torch.Tensor, out: torch.Tensor, scale: float, partition_size: int = 0,
+                   workspace: Optional[torch.Tensor] = None,
+                   slot_mapping: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step in one launch: pa_append_kv (``k_new``/``v_new``
+    ``[num_seqs, Hkv, D]`` to each sequence's newest slot, the slots to
+    ``slot_mapping`` if given) followed by pa_decode, bit for bit."""
+    lib = load_library()
+    _validate_seqs(pool, seqs)
+    S, Hq, D = q.shape
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must have q's shape")
+    _, _, H, Dp, _ = _pool_geometry(pool.k_cache, pool.v_cache, pool.layout)
+    if D != Dp:
+        raise ValueError("q's head_dim differs from the pool's")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (S, H, D):
+            raise ValueError(f"{name} must be [{S}, {H}, {D}], got {tuple(t.shape)}")
+    if slot_mapping is not None and tuple(slot_mapping.shape) != (S,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    sm = None if slot_mapping is None else _dev(slot_mapping, "slot_mapping", torch.int64)
+    cp, cs = pool.c(), seqs.c()
+    st = lib.pa_decode_step(ctypes.byref(cp), ctypes.byref(cs), _dev(k_new, "k_new", pool.dtype),
+                            _dev(v_new, "v_new", pool.dtype), sm, _dev(q, "q", pool.dtype),
+                            _dev(out, "out", pool.dtype), Hq, float(scale), int(partition_size),
+                            ws_ptr, ws_bytes, _stream(stream))
+    _check("pa_decode_step", st)
+    return out
+
+
 def pa_decode_noalloc(pool: KVPool, seqs: SeqDesc, q: torch.Tensor, out: torch.Tensor,
                       scale: float, partition_size: int = 0, stream=None) -> torch.Tensor:
     """pa_decode without a workspace: the split's counters and partial
@@ -620,7 +655,7 @@ def pa_version() -> int:
 __all__ = [
     "LIB_PATH", "EXPORTED", "PaKVPool", "PaSeqDesc", "PagedAttentionError", "KVPool", "SeqDesc",
     "load_library", "status_name", "pa_slot_mapping", "pa_write_kv", "pa_decode_workspace_bytes",
-    "decode_workspace", "pa_decode", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit",
+    "decode_workspace", "pa_decode", "pa_decode_step", "pa_prefill", "pa_decode_split_info", "PaDecodeSplit",
     "pa_decode_noalloc", "BlockAllocator", "pa_copy_blocks", "pa_read_checksum",
     "host_pool_c", "pa_swap_blocks", "paged_attention", "pa_append_kv", "check_tables", "check_slots",
     "validating", "PA_SWAP_OUT", "PA_SWAP_IN", "PA_LAYOUT_TOKEN_MAJOR",

@@ -296,7 +296,17 @@ __device__ __forceinline__ void merge_pair(const DecodeArgs& a, int s, int g, in
 //
 // Plan in dynamic LDS: ctx[S] clamped context lengths, pre[S+1] exclusive
 // prefix sum of blocks per KV head.
-template <typename T, int D, int R, bool kSmall>
+//
+// kStep: the decode step in one launch (pa_decode_step).  Each sequence's
+// new token (position context_lens[s] - 1) is written to its slot by one
+// workgroup, exactly as pa_append_kv writes it, and its slot recorded.
+// The wave whose 16-token unit holds that position does not read the row
+// back from the pool: its loads of that row are pointed past their
+// descriptor (no memory access) and the row's fragments come from k_new and
+// v_new instead, loaded when the segment starts.  No location is then both
+// written and read in one call, and the result equals pa_append_kv followed
+// by pa_decode bit for bit.
+template <typename T, int D, int R, bool kSmall, bool kStep>
 __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(DecodeArgs a) {
   constexpr int kWaves = decode_waves<T, D, R>();
   constexpr int kThreads = 64 * kWaves;
@@ -316,6 +326,8 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
   __shared__ int sm_last[2];
   __shared__ int sm_nb[kWaves][2];   // per wave: least and most blocks of a non-empty pair
   __shared__ int sm_unit;
+  // kStep: 1 where the sequence's new token lies inside its clamped context
+  __shared__ uint8_t sm_new[kStep ? kMaxDecodeSeqs : 1];
 
   const int S = a.num_seqs;
   const int Hkv = a.num_kv_heads;
@@ -336,6 +348,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     int nb_lo = 0x7fffffff, nb_hi = 0;
     for (int q = b0; q < b1; ++q) {
       int L = a.context_lens[q];
+      if constexpr (kStep) sm_new[q] = L >= 1 && L <= a.context_cap;
       L = L < 0 ? 0 : (L > a.context_cap ? a.context_cap : L);
       sm_ctx[q] = L;
       const int nbq = (L + kUnit - 1) / kUnit;
@@ -531,6 +544,24 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       int2 tbl = load_tbl(cur, c0);
       uint32_t qv[N][NW];
       load_q(cur, qv);
+      // kStep: the unit of the segment that holds its pair's new token (-1:
+      // none), the token's row in that unit, and the row's fragments
+      int newj = -1, newt = 0;
+      F knew, vnew;
+      auto step_row = [&](const Seg& x) {
+        newj = -1;
+        if constexpr (kStep) {
+          const int jn = (x.L - 1) >> 4;
+          if (sm_new[x.s] && jn >= x.blk0 && jn < x.blk1) {
+            newj = jn;
+            newt = (x.L - 1) & 15;
+            const int64_t o = ((static_cast<int64_t>(x.s) * Hkv + x.g) * D + li * EPL) * LT::kElt;
+            knew = load_frag<NW>(static_cast<const char*>(a.k_new) + o);
+            vnew = load_frag<NW>(static_cast<const char*>(a.v_new) + o);
+          }
+        }
+      };
+      step_row(cur);
       uint32_t lane_off = cur.g * head_bytes + li * EPL * LT::kElt + row * row_bytes;
       auto chunk_blocks = [&](const Seg& x, int cs) {
         const int ce = min(x.blk1, cs + kChunkBlocks);
@@ -555,8 +586,10 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
         int phys = -1, phys2 = -1;
         int nvalid = 0;
         int sub = 0;                     // first token row of the unit inside its block
+        bool has_new = false;            // kStep: the unit holds the pair's new token
         if (k < nk) {
           const int j = c0 + wave + kWaves * k;
+          if constexpr (kStep) has_new = j == newj;
           phys = __builtin_amdgcn_readlane(tbl.x, k);
           phys2 = small ? __builtin_amdgcn_readlane(tbl.y, k) : phys;
           const int n = cur.tok1 - j * kUnit;
@@ -575,19 +608,33 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
         const Rsrc rk2 = small ? make_rsrc(kpool + off2, ok2 ? block_bytes : 0u) : rk;
         const Rsrc rv2 = small ? make_rsrc(vpool + off2, ok2 ? block_bytes : 0u) : rv;
         const uint32_t lane_off2 = small ? lane_off - 8 * row_bytes : lane_off;
+        uint32_t offs[4];
+    #pragma unroll
+        for (int uu = 0; uu < 4; ++uu) offs[uu] = (uu < 2 ? lane_off : lane_off2) + uu * 4 * row_bytes;
+        if constexpr (kStep) {
+          // the new token's row (lanes of row newt mod 4, fragment newt / 4) is
+          // not read: an offset at the descriptor's size loads zeros, touching
+          // nothing
+          if (has_new && row == (newt & 3)) {
+            const uint32_t past2 = small ? (ok2 ? block_bytes : 0u) : size;
+    #pragma unroll
+            for (int uu = 0; uu < 4; ++uu)
+              if (uu == (newt >> 2)) offs[uu] = uu < 2 ? size : past2;
+          }
+        }
     #pragma unroll
         for (int uu = 0; uu < 2; ++uu)
-          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, lane_off + uu * 4 * row_bytes);
+          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk, offs[uu]);
     #pragma unroll
         for (int uu = 2; uu < 4; ++uu)
-          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, lane_off2 + uu * 4 * row_bytes);
+          kf[uu] = load_frag_buf<NW, kKVPolicy>(rk2, offs[uu]);
     #pragma unroll
         for (int uu = 0; uu < 2; ++uu)
-          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, lane_off + uu * 4 * row_bytes);
+          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv, offs[uu]);
     #pragma unroll
         for (int uu = 2; uu < 4; ++uu)
-          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, lane_off2 + uu * 4 * row_bytes);
-        return vmask;
+          vf[uu] = load_frag_buf<NW, kKVPolicy>(rv2, offs[uu]);
+        return has_new ? (vmask | 0x10000) : vmask;
       };
 
       // Online softmax over one block (JuliaPagedAttn "Online Softmax"): scores,
@@ -596,6 +643,19 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
       // are rescaled); in between, weights exp2(z - m) may exceed 1 (up to
       // 2^kRescaleLog2), which leaves sum(w v) / sum(w) unchanged.
       auto process = [&](F (&kf)[4], F (&vf)[4], int vmask) {
+        if constexpr (kStep) {
+          // the unit holding the new token: its row from k_new / v_new
+          if (vmask & 0x10000) {
+    #pragma unroll
+            for (int uu = 0; uu < 4; ++uu) {
+              if (uu == (newt >> 2) && row == (newt & 3)) {
+                kf[uu] = knew;
+                vf[uu] = vnew;
+              }
+            }
+          }
+          vmask &= 0xffff;
+        }
         float z[4];
     #pragma unroll
         for (int uu = 0; uu < 4; ++uu) {
@@ -829,6 +889,7 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
         }
         tbl = tbl_nxt;
         load_q(cur, qv);
+        step_row(cur);
         tbl_nxt = has_next ? load_tbl(nxt, nxt.blk0) : make_int2(-1, -1);
         c0 = cur.blk0;
         nk = chunk_blocks(cur, c0);
@@ -908,6 +969,42 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
     __syncthreads();
     if (u >= up.U) break;
   }
+  // ---- kStep: the new token of sequences blockIdx.x, + grid, ... to its slot,
+  // by pa_append_kv's rule (position L - 1 of the raw length; none for an
+  // empty context, a position past the table, or an entry outside the pool).
+  // Nothing in the call reads these rows, so the workgroup writes them when
+  // its own units are done, off the path of its first loads.
+  if constexpr (kStep) {
+    const uint32_t bsh = a.geom.block_shift;
+    const int head_bytes_ = D * static_cast<int>(sizeof(T));
+    const int chunks = a.num_kv_heads * head_bytes_ / 16;     // 16-byte chunks of one row
+    for (int q = blockIdx.x; q < S; q += gridDim.x) {
+      const int pos = a.context_lens[q] - 1;
+      int64_t slot = -1;
+      if (pos >= 0 && (pos >> bsh) < a.max_blocks_per_seq) {
+        const int phys =
+            a.block_tables[static_cast<int64_t>(q) * a.max_blocks_per_seq + (pos >> bsh)];
+        if (phys >= 0 && phys < a.num_blocks)
+          slot = (static_cast<int64_t>(phys) << bsh) + (pos & ((1 << bsh) - 1));
+      }
+      if (tid == 0 && a.slot_mapping != nullptr) a.slot_mapping[q] = slot;
+      for (int i = tid; slot >= 0 && i < 2 * chunks; i += kThreads) {
+        const bool is_v = i >= chunks;
+        const int c = is_v ? i - chunks : i;
+        const int hh = c / (head_bytes_ / 16);
+        const int cq = c - hh * (head_bytes_ / 16);
+        const uint4 val = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new)
+            [static_cast<int64_t>(q) * chunks + c];
+        const int64_t blk = slot >> bsh;
+        const int64_t dst = blk * a.geom.block_stride +
+                            static_cast<int64_t>(slot - (blk << bsh)) * a.geom.token_stride +
+                            static_cast<int64_t>(hh) * a.geom.head_stride + 16 * cq;
+        char* pool = static_cast<char*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache));
+        *reinterpret_cast<uint4*>(pool + dst) = val;
+      }
+    }
+  }
+
   // the last workgroup to finish leaves both counters at zero for the next call
   // (every other workgroup has taken its last unit by then)
   if (split && up.U > up.G && tid == 0) {
@@ -921,10 +1018,10 @@ __global__ __launch_bounds__((64 * decode_waves<T, D, R>())) void decode_kernel(
 
 // The persistent grid: what the device holds at once, but no more
 // workgroups than there are slices (split) or pairs (whole pairs).
-template <typename T, int D, int R, bool kSmall>
+template <typename T, int D, int R, bool kSmall, bool kStep>
 hipError_t grid_typed(const DecodeArgs& a, int* grid) {
   const size_t lds = plan_lds_bytes(a.num_seqs);
-  const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R, kSmall>);
+  const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, R, kSmall, kStep>);
   int resident = 0;
   constexpr int kThreads = 64 * decode_waves<T, D, R>();
   hipError_t e = resident_workgroups(fn, kThreads, lds, &resident);
@@ -936,29 +1033,36 @@ hipError_t grid_typed(const DecodeArgs& a, int* grid) {
   return hipSuccess;
 }
 
-template <typename T, int D, int R, bool kSmall>
+template <typename T, int D, int R, bool kSmall, bool kStep>
 hipError_t run_typed(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   int grid = 0;
-  const hipError_t e = grid_typed<T, D, R, kSmall>(a, &grid);
+  const hipError_t e = grid_typed<T, D, R, kSmall, kStep>(a, &grid);
   if (e != hipSuccess) return e;
   if (grid_only != nullptr) {
     *grid_only = grid;
     return hipSuccess;
   }
   constexpr int kThreads = 64 * decode_waves<T, D, R>();
-  return launch_kernel(decode_kernel<T, D, R, kSmall>, dim3(grid), dim3(kThreads),
+  return launch_kernel(decode_kernel<T, D, R, kSmall, kStep>, dim3(grid), dim3(kThreads),
                        plan_lds_bytes(a.num_seqs), stream, a);
 }
 
-template <typename T, int D, bool kSmall>
-hipError_t run_heads(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
+template <typename T, int D, bool kSmall, bool kStep>
+hipError_t run_heads_step(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return run_typed<T, D, 0, kSmall>(a, stream, grid_only);
-    case 2: return run_typed<T, D, 1, kSmall>(a, stream, grid_only);
-    case 4: return run_typed<T, D, 2, kSmall>(a, stream, grid_only);
-    case 8: return run_typed<T, D, 3, kSmall>(a, stream, grid_only);
+    case 1: return run_typed<T, D, 0, kSmall, kStep>(a, stream, grid_only);
+    case 2: return run_typed<T, D, 1, kSmall, kStep>(a, stream, grid_only);
+    case 4: return run_typed<T, D, 2, kSmall, kStep>(a, stream, grid_only);
+    case 8: return run_typed<T, D, 3, kSmall, kStep>(a, stream, grid_only);
     default: return hipErrorInvalidValue;
   }
+}
+
+// pa_decode_step (k_new set) runs the kStep variant
+template <typename T, int D, bool kSmall>
+hipError_t run_heads(const DecodeArgs& a, hipStream_t stream, int* grid_only) {
+  return a.k_new != nullptr ? run_heads_step<T, D, kSmall, true>(a, stream, grid_only)
+                            : run_heads_step<T, D, kSmall, false>(a, stream, grid_only);
 }
 
 // Blocks of 8 tokens hold half a 16-token unit: a variant of their own.

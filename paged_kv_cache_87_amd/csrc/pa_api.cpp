@@ -450,6 +450,22 @@ pa_status prepare_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const 
   return PA_OK;
 }
 
+// pa_decode and pa_decode_step: the caller's workspace, then the launch
+pa_status decode_with_workspace(pa::DecodeArgs& a, const pa::DecodePlan& plan, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                  plan.workspace_bytes, workspace == nullptr ? size_t(0) : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    a.counters = static_cast<int32_t*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_offset);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
+  }
+  return hip_status(pa::launch_decode(a, stream), "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -464,17 +480,28 @@ pa_status pa_decode(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void*
                                       true, &a, &plan);
   if (st != PA_OK) return st;
   if (seqs->num_seqs == 0) return PA_OK;
-  if (plan.workspace_bytes > 0) {
-    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
-                  plan.workspace_bytes, workspace == nullptr ? size_t(0) : workspace_bytes);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    a.counters = static_cast<int32_t*>(workspace);
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_offset);
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_ml_offset);
-  }
-  return hip_status(pa::launch_decode(a, stream), "decode launch");
+  return decode_with_workspace(a, plan, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_step(const pa_kv_pool* pool, const pa_seq_desc* seqs, const void* k_new,
+                         const void* v_new, int64_t* slot_mapping, const void* q, void* out,
+                         int32_t num_q_heads, float scale, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  pa::DecodeArgs a;
+  pa::DecodePlan plan;
+  const pa_status st = prepare_decode(pool, seqs, q, out, num_q_heads, scale, partition_size,
+                                      true, &a, &plan);
+  if (st != PA_OK) return st;
+  if (seqs->num_seqs == 0) return PA_OK;
+  if (k_new == nullptr || v_new == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "k_new or v_new is null");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  return decode_with_workspace(a, plan, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -121,6 +121,9 @@ struct DecodeArgs {
   float* part_o;           // [2 * max_slices, n_rep, head_dim] partial outputs
   float* part_ml;          // [2 * max_slices, n_rep, 2] their (max, sum)
   int32_t* counters;       // [num_seqs * num_kv_heads] arrivals, zero between calls
+  const void* k_new;       // decode step only (else null): [num_seqs, num_kv_heads, head_dim]
+  const void* v_new;       //   new K / V rows, written to their slots and attended from here
+  int64_t* slot_mapping;   //   their slots, written (may be null)
   int32_t num_seqs;
   int32_t num_blocks;
   int32_t num_kv_heads;

@@ -147,6 +147,13 @@ class GpuStep:
         """Decode step's slot mapping and write in one launch."""
         pa.pa_append_kv(self.pool, self.seqs, self.new_k, self.new_v, self.slots)
 
+    def decode_step(self):
+        """Decode step in one launch: the write of the new token's K/V and the
+        decode (pa_decode_step)."""
+        w = self.w
+        return pa.pa_decode_step(self.pool, self.seqs, self.new_k, self.new_v, self.q, self.out,
+                                 w.scale, self.partition_size, self.workspace, self.slots)
+
     def attend(self, partition_size=None):
         w = self.w
         if w.kind == "decode":
