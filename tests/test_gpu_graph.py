@@ -109,3 +109,34 @@ def test_prefill_step_replays_in_a_graph(dtype):
         torch.cuda.synchronize()
         assert np.array_equal(g.slots.cpu().numpy(), slots_ref), f"replay {i} slots"
         assert torch.equal(g.out.view(bits), want.view(bits)), f"replay {i}"
+
+
+@pytest.mark.parametrize("partition_size", [0, 256])
+def test_one_launch_decode_step_replays_in_a_graph(partition_size):
+    """pa_decode_step (the write and the decode in one launch) captured and
+    replayed: outputs and slots bit for bit like the eager step."""
+    w = _workload(partition_size)
+    announce(f"{w.name} one-launch step graph capture")
+    g = runner.GpuStep(w)
+    g.write_history()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.decode_step()
+    torch.cuda.synchronize()
+    want, slots = g.out.clone(), g.slots.clone()
+    _, _, slots_ref, ref = oracle_step(w)
+    assert np.array_equal(slots.cpu().numpy(), slots_ref)
+    assert_close(want.float().cpu().numpy().astype(np.float64), ref, w.dtype, w.name + " eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        g.decode_step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        g.out.fill_(float("nan"))
+        g.slots.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g.slots, slots), f"replay {i} slots"
+        assert torch.equal(g.out.view(torch.int16), want.view(torch.int16)), f"replay {i}"
