@@ -2,8 +2,8 @@
 write (pa_append_kv) followed by the split decode, with the caller's
 workspace (pa_decode) or with the library's own array (pa_decode_noalloc).
 Prefill: slot mapping, K/V write and the causal prefill of a mixed batch
-(decode rows, continuations and whole prompts), bf16 and fp32.  None of them
-records a memset or an allocation, and the decode leaves its counters at zero
+(decode rows, continuations and whole prompts), bf16 and fp32.  And the
+decode step in one launch (pa_decode_step).  None of them records a memset or an allocation, and the decode leaves its counters at zero
 after every call, so a replayed step must equal the eager step bit for bit.
 Between replays the program does eager work of its own (the output is
 poisoned) and synchronises; every replay is checked, and so is the oracle on
