@@ -276,3 +276,26 @@ def test_read_checksum_rejects_bad_arguments(lib):
     assert lib.pa_read_checksum(FAKE, 64, words, 65536, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_read_checksum(FAKE, (2 << 30) + 16, words, 1, None) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_last_error() != b""
+
+
+def step(lib, p, s, k=FAKE, v=FAKE, hq=8, part=0, ws=None, ws_bytes=0):
+    return lib.pa_decode_step(ctypes.byref(p), ctypes.byref(s), k, v, None, FAKE, FAKE, hq, 0.1,
+                              part, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), pa.PA_ERR_INVALID_ARG),
+    (dict(v=None), pa.PA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), pa.PA_ERR_INVALID_ARG),             # not 16-byte aligned
+    (dict(hq=5), pa.PA_ERR_INVALID_ARG),                   # the decode's own checks
+    (dict(part=16), pa.PA_ERR_WORKSPACE),
+])
+def test_decode_step_rejects_bad_arguments(lib, kw, status):
+    """pa_decode_step checks the write's arguments and the decode's before
+    anything is launched (no device is touched here)."""
+    assert step(lib, pool(), seqs(), **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_decode_step_empty_batch_enqueues_nothing(lib):
+    assert step(lib, pool(), seqs(num_seqs=0), k=None, v=None) == pa.PA_OK
