@@ -19,8 +19,9 @@ second), the decode call's roofline (K/V bytes / decode kernel time against
 whole step of the same workload, and secondary measurements of the
 batched causal prefill (TFLOP/s against 2.5 PFLOP/s bf16), of the
 long-context shared-prefix decode, of the copy-on-write block copy and of
-the block swap between the device pool and a pinned host pool, and the
-decode step in one launch (pa_decode_step) against the two-launch step.
+the block swap between the device pool and a pinned host pool, the fp32
+prefill on GPT-2 shapes (against the fp32 matrix peak), and the decode step
+in one launch (pa_decode_step) against the two-launch step.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200]
     python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
@@ -45,6 +46,7 @@ if ROOT not in sys.path:
 PCIE5_X16_GBPS = 63.0   # 32 GT/s x 16 lanes, 128b/130b coding, one direction
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+F32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = "paged-attn decode μs/step + KV-read HBM GB/s (% of peak), batch 64 ctx 4096"
 
 
@@ -370,6 +372,31 @@ def secondary(torch, np, stream, K, W, partition_size):
         "us_per_step": step_ms * 1e3, "prefill_us": pre * 1e3,
         "flops": flops, "tflops": flops / (pre * 1e-3) / 1e12,
         "frac_bf16_peak": flops / (pre * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+    }
+    del g
+    torch.cuda.empty_cache()
+    # the fp32 prefill on GPT-2-shaped prompts: 12 heads of 64 (MHA), 16 prompts
+    # U[256, 2048], on the fp32 matrix cores
+    rng = np.random.default_rng(87007)
+    plens = [int(x) for x in rng.integers(256, 2049, size=16)]
+    w = wl.prefill_workload("gpt2_prefill_f32", 87007, dtype=wl.F32, num_q_heads=12,
+                            num_kv_heads=12, head_dim=64, block_size=16,
+                            num_blocks=sum((x + 15) // 16 for x in plens) + 16,
+                            context_lens=plens, pool_fill="zero")
+    g = runner.GpuStep(w)
+    g.write_history()
+    step_ms, pre_ms = timed(torch, stream, K, W, lambda: (g.slot_mapping(), g.write()), g.attend,
+                            settle=True)
+    lens = w.context_lens.astype(np.int64)
+    flops = 2.0 * w.num_q_heads * w.head_dim * float(np.sum(lens * (lens + 1)))
+    pre = float(np.mean(pre_ms))
+    out["batched_prefill_f32"] = {
+        "config": {"batch": w.num_seqs, "num_q_heads": 12, "num_kv_heads": 12, "head_dim": 64,
+                   "prompt_lens": "uniform [256, 2048], seed 87007",
+                   "total_tokens": int(lens.sum())},
+        "us_per_step": step_ms * 1e3, "prefill_us": pre * 1e3, "flops": flops,
+        "tflops": flops / (pre * 1e-3) / 1e12,
+        "frac_f32_mfma_peak": flops / (pre * 1e-3) / 1e12 / F32_MFMA_PEAK_TFLOPS,
     }
     del g
     torch.cuda.empty_cache()
